@@ -1,0 +1,307 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: top-k index rows bit-exact (integer-valued indexer inputs make every
+score exact and the tie rule makes the set unique); outputs within max-abs
+1e-4 for float32 workloads and 2e-2 for bf16 workloads (the oracle reads the
+same bf16-rounded values and accumulates in float64).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+from top_sparse_attention_indexer_amd import binding as B
+from top_sparse_attention_indexer_amd import synth
+from top_sparse_attention_indexer_amd.tensors import to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_fused(w, x, use_gate=True, use_route=True, want_idx=True, softmax_scale=0.0):
+    p = B.problem_for(w, softmax_scale)
+    dev = to_device(w, x)
+    out = torch.empty((w.batch, w.n_q, w.h_q, w.head_dim), dtype=torch.float32, device="cuda")
+    idx = (torch.full((w.batch, w.n_q, w.top_k), -7, dtype=torch.int32, device="cuda")
+           if want_idx else None)
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    B.dsa_fused_forward(p, dev["q_idx"], dev["k_idx"], dev["q"], dev["k"], dev["v"],
+                        dev["gate"] if use_gate else None, dev["y2"] if use_gate else None,
+                        dev["route"] if use_route else None, out, idx, ws)
+    torch.cuda.synchronize()
+    return out, idx
+
+
+def check_rows(w, x, out, idx, rows, use_gate=True, use_route=True, batches=None):
+    """Oracle on the chosen rows; exact index rows, outputs within tolerance."""
+    bs = list(range(w.batch)) if batches is None else batches
+    want_out, want_idx = O.forward(w, x, rows=rows, batches=bs, use_gate=use_gate,
+                                   use_route=use_route)
+    got_out = out[bs][:, rows].cpu().numpy() if not isinstance(out, np.ndarray) else out
+    if idx is not None:
+        got_idx = idx[bs][:, rows].cpu().numpy()
+        bad = np.argwhere(np.any(got_idx != want_idx, axis=-1))
+        assert bad.size == 0, f"index rows differ at (batch, row-sample) {bad[:5].tolist()}"
+    err = np.max(np.abs(got_out.astype(np.float64) - want_out))
+    assert err <= TOL[w.qkv_dtype], f"max-abs error {err}"
+    return err
+
+
+def check_index_structure(w, idx):
+    """Every row: ascending ids in [0, p], count min(K, vis), then -1 padding."""
+    N, L, K = w.n_q, w.kv_len, w.top_k
+    vis = torch.arange(N, device="cuda", dtype=torch.int64) + (L - N + 1)
+    cnt = torch.clamp(vis, max=K)
+    pos = torch.arange(K, device="cuda")
+    for b in range(w.batch):
+        t = idx[b].to(torch.int64)
+        valid = pos[None, :] < cnt[:, None]
+        assert torch.all(torch.where(valid, t >= 0, t == -1)).item()
+        assert torch.all(torch.where(valid, t < vis[:, None], True)).item()
+        d = t[:, 1:] - t[:, :-1]
+        both = valid[:, 1:]
+        assert torch.all(torch.where(both, d > 0, True)).item()
+
+
+# --------------------------------------------------------------------------- the five workloads
+def test_tiny_prefill_fp32_all_rows(announce):
+    w = synth.WORKLOADS["tiny_prefill_fp32"]
+    x = synth.make_inputs(w)
+    announce(f"fused_forward {w}")
+    out, idx = run_fused(w, x)
+    check_rows(w, x, out, idx, rows=list(range(w.n_q)))
+
+
+def test_decode_b8_ctx128k_all_rows(announce):
+    w = synth.WORKLOADS["decode_b8_ctx128k"]
+    x = synth.make_inputs(w)
+    announce(f"fused_forward {w}")
+    out, idx = run_fused(w, x)
+    check_rows(w, x, out, idx, rows=[0])
+
+
+def test_decode_ctx1m_mqa_all_rows(announce):
+    w = synth.WORKLOADS["decode_ctx1m_mqa"]
+    x = synth.make_inputs(w)
+    announce(f"fused_forward {w}")
+    out, idx = run_fused(w, x)
+    check_rows(w, x, out, idx, rows=[0])
+    # planted rows are selected exactly when their score clears the threshold
+    s = O.indexer_scores(x["q_idx"][0, 0], x["k_idx"][0], w.kv_len)
+    sel = set(idx[0, 0].cpu().numpy().tolist())
+    thr = s[sorted(sel)].min()
+    for j in x["planted"]:
+        if s[j] > thr:
+            assert int(j) in sel
+        elif s[j] < thr:
+            assert int(j) not in sel
+
+
+def test_prefill_32k_sampled_rows(announce):
+    w = synth.WORKLOADS["prefill_32k"]
+    x = synth.make_inputs(w)
+    announce(f"fused_forward {w}")
+    out, idx = run_fused(w, x)
+    check_index_structure(w, idx)
+    rows = synth.sample_rows(w, 64).tolist()
+    announce(f"oracle on {len(rows)} sampled rows")
+    check_rows(w, x, out, idx, rows=rows)
+
+
+def test_elastic_prefill_64k_sampled_rows(announce):
+    w = synth.WORKLOADS["elastic_prefill_64k"]
+    x = synth.make_inputs(w)
+    assert 0 < x["route"].sum() < x["route"].size     # both routes present
+    announce(f"fused_forward {w}")
+    out, idx = run_fused(w, x)
+    rows = synth.sample_rows(w, 12).tolist()
+    announce(f"oracle on {len(rows)} sampled rows x 2 sequences")
+    check_rows(w, x, out, idx, rows=rows)
+    del out, idx
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- edge cases, small shapes
+def _w(B_, N, L, Hq, Hkv, d, didx, K, dt="bf16", route_p=None, seed=11):
+    rng = (-4, 4) if dt == "bf16" else (-8, 8)
+    return synth.Workload("edge", B_, N, L, Hq, Hkv, d, didx, K, dt, dt, rng,
+                          route_sparse_p=route_p, seed=seed)
+
+
+EDGE = [
+    ("chunk_N_lt_L", _w(2, 100, 1000, 8, 2, 128, 64, 64)),
+    ("K_ge_L", _w(1, 64, 64, 4, 1, 64, 32, 128)),
+    ("K_eq_vis_boundary", _w(1, 40, 100, 4, 2, 64, 32, 70)),
+    ("K_1", _w(2, 33, 77, 4, 4, 128, 16, 1)),
+    ("ragged_decode_8193", _w(3, 1, 8193, 8, 2, 128, 64, 256)),
+    ("ragged_decode_24577_spec3", _w(2, 3, 24577, 16, 2, 64, 128, 512)),
+    ("decode_8_rows", _w(1, 8, 20000, 4, 1, 128, 64, 300)),
+    ("prefill_9_rows_fp32", _w(1, 9, 3000, 4, 2, 128, 32, 200, dt="fp32")),
+    ("mixed_route", _w(2, 70, 300, 8, 2, 128, 64, 32, route_p=0.5, seed=5)),
+    ("fp32_d64", _w(1, 130, 130, 6, 3, 64, 64, 17, dt="fp32")),
+    ("mqa_decode_many_heads", _w(1, 1, 50000, 64, 1, 128, 64, 2048)),
+]
+
+
+@pytest.mark.parametrize("name,w", EDGE, ids=[e[0] for e in EDGE])
+@pytest.mark.parametrize("use_gate", [True, False])
+def test_edge_shapes(name, w, use_gate, announce):
+    x = synth.make_inputs(w)
+    announce(f"fused_forward {name} gate={use_gate} {w}")
+    out, idx = run_fused(w, x, use_gate=use_gate)
+    rows = list(range(w.n_q)) if w.n_q <= 80 else synth.sample_rows(w, 40).tolist()
+    check_rows(w, x, out, idx, rows=rows, use_gate=use_gate)
+
+
+def test_all_dense_route_skips_indexer(announce):
+    w = _w(2, 50, 200, 4, 2, 128, 64, 16)
+    x = synth.make_inputs(w)
+    x["route"][:] = 0
+    x["route"][1, 2] = 1      # sequence 1 keeps one sparse head
+    announce(f"fused_forward all-dense seq 0 {w}")
+    out, idx = run_fused(w, x)
+    assert torch.all(idx[0] == -1).item()
+    check_rows(w, x, out, idx, rows=list(range(w.n_q)))
+
+
+def test_custom_softmax_scale(announce):
+    w = _w(1, 20, 90, 4, 1, 64, 32, 10, dt="fp32")
+    x = synth.make_inputs(w)
+    announce("fused_forward softmax_scale=0.05")
+    out, idx = run_fused(w, x, softmax_scale=0.05)
+    want, _ = O.forward(w, x, softmax_scale=0.05)
+    assert np.max(np.abs(out.cpu().numpy() - want)) <= 1e-4
+
+
+def test_gate_end_points_exact(announce):
+    w = _w(1, 12, 60, 4, 2, 128, 64, 8)
+    x = synth.make_inputs(w)
+    x1 = dict(x, gate=np.ones_like(x["gate"]))
+    announce("fused_forward gate=1 vs no gate")
+    a1, _ = run_fused(w, x1)
+    a, _ = run_fused(w, x, use_gate=False)
+    assert torch.equal(a1, a)
+    x0 = dict(x, gate=np.zeros_like(x["gate"]))
+    a0, _ = run_fused(w, x0)
+    assert np.array_equal(a0.cpu().numpy(), x["y2"])
+
+
+def test_deterministic_repeat(announce):
+    w = synth.WORKLOADS["decode_b8_ctx128k"].replace(kv_len=40000)
+    x = synth.make_inputs(w)
+    announce("fused_forward x3 determinism")
+    o1, i1 = run_fused(w, x)
+    o2, i2 = run_fused(w, x)
+    o3, i3 = run_fused(w, x)
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+    assert torch.equal(i1, i2) and torch.equal(i1, i3)
+
+
+# --------------------------------------------------------------------------- single entry points
+@pytest.mark.parametrize("N,L,didx,dt", [(1, 5000, 64, "bf16"), (5, 777, 32, "fp32"),
+                                          (100, 333, 64, "bf16"), (64, 64, 128, "fp32")])
+def test_indexer_scores_entry(N, L, didx, dt, announce):
+    w = _w(2, N, L, 4, 1, 64, didx, 8, dt=dt)
+    x = synth.make_inputs(w, parts=("q_idx", "k_idx"))
+    dev = to_device(w, x)
+    p = B.problem_for(w)
+    scores = torch.empty((2, N, L), dtype=torch.float32, device="cuda")
+    announce(f"indexer_scores N={N} L={L} didx={didx} {dt}")
+    B.dsa_indexer_scores(p, dev["q_idx"], dev["k_idx"], scores)
+    got = scores.cpu().numpy()
+    for b in range(2):
+        for n in range(N):
+            vis = O.visible_count(n, N, L)
+            want = O.indexer_scores(x["q_idx"][b, n], x["k_idx"][b], vis)
+            assert np.array_equal(got[b, n, :vis].astype(np.float64), want)
+            assert np.all(np.isneginf(got[b, n, vis:]))
+
+
+def _adversarial_rows(L, rng):
+    rows = [np.zeros(L, np.float32),                       # all equal
+            np.arange(L, dtype=np.float32),                # s_j = j
+            -np.arange(L, dtype=np.float32),               # s_j = -j
+            np.where(rng.random(L) < 0.5, -0.0, 0.0).astype(np.float32),   # signed zeros
+            rng.integers(-3, 4, size=L).astype(np.float32)]
+    peaks = np.full(L, -5.0, np.float32)                   # maxima on chunk boundaries
+    for j in range(0, L, 8192):
+        peaks[j] = 9.0
+        if j > 0:
+            peaks[j - 1] = 9.0
+    rows.append(peaks)
+    rows.append(rng.standard_normal(L).astype(np.float32))  # non-integer scores
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("L,K", [(40000, 2048), (20000, 1), (3000, 2999), (3000, 3000),
+                                  (3000, 3001), (16384, 8192)])
+@pytest.mark.parametrize("n_rows", [7, 1, 9])      # split-row path (<= 8 rows), rows path (9)
+def test_topk_entry_adversarial(L, K, n_rows, announce):
+    rng = np.random.default_rng(L + K)
+    base = _adversarial_rows(L, rng)
+    extra = rng.integers(-2, 3, size=(max(0, n_rows - base.shape[0]), L)).astype(np.float32)
+    rows = np.concatenate([base, extra])[:n_rows]
+    w = _w(1, n_rows, L, 4, 1, 64, 32, K)
+    sc = np.full((1, n_rows, L), -np.inf, np.float32)
+    for n in range(n_rows):
+        vis = O.visible_count(n, n_rows, L)
+        sc[0, n, :vis] = rows[n, :vis]
+    p = B.problem_for(w)
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    idx = torch.full((1, n_rows, K), -7, dtype=torch.int32, device="cuda")
+    announce(f"topk L={L} K={K} rows={n_rows}")
+    B.dsa_topk(p, torch.from_numpy(sc).cuda(), idx, ws)
+    got = idx.cpu().numpy()
+    for n in range(n_rows):
+        vis = O.visible_count(n, n_rows, L)
+        want = O.select_top_k(sc[0, n, :vis].astype(np.float64), K)
+        assert np.array_equal(got[0, n], want), f"row {n}"
+
+
+def test_topk_entry_many_rows(announce):
+    """The one-row-per-workgroup path (N > 8) on prefill-shaped scores."""
+    w = _w(2, 300, 5000, 4, 1, 64, 64, 700)
+    x = synth.make_inputs(w, parts=("q_idx", "k_idx"))
+    sc = np.full((2, 300, 5000), -np.inf, np.float32)
+    for b in range(2):
+        for n in range(300):
+            vis = O.visible_count(n, 300, 5000)
+            sc[b, n, :vis] = O.indexer_scores(x["q_idx"][b, n], x["k_idx"][b], vis)
+    p = B.problem_for(w)
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((2, 300, 700), dtype=torch.int32, device="cuda")
+    announce("topk many rows")
+    B.dsa_topk(p, torch.from_numpy(sc).cuda(), idx, ws)
+    got = idx.cpu().numpy()
+    for b in range(2):
+        for n in range(0, 300, 7):
+            vis = O.visible_count(n, 300, 5000)
+            assert np.array_equal(got[b, n], O.select_top_k(sc[b, n, :vis].astype(np.float64), 700))
+
+
+@pytest.mark.parametrize("N,L,K,route_p", [(1, 9000, 512, None), (40, 600, 64, 0.5),
+                                            (4, 3000, 100, 0.5)])
+def test_sparse_attn_entry_with_oracle_indices(N, L, K, route_p, announce):
+    w = _w(2, N, L, 8, 2, 128, 64, K, route_p=route_p)
+    x = synth.make_inputs(w)
+    want_out, want_idx = O.forward(w, x)
+    dev = to_device(w, x)
+    p = B.problem_for(w)
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    idx = torch.from_numpy(want_idx.astype(np.int32)).cuda()
+    out = torch.empty((2, N, 8, 128), dtype=torch.float32, device="cuda")
+    announce(f"sparse_attn N={N} L={L} K={K}")
+    B.dsa_sparse_attn(p, dev["q"], dev["k"], dev["v"], idx, dev["gate"], dev["y2"], dev["route"],
+                      out, ws)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(out.cpu().numpy() - want_out)) <= TOL["bf16"]

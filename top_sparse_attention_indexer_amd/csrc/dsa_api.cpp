@@ -1,0 +1,316 @@
+// C ABI of libdsa: argument checks, workspace planning and kernel dispatch.
+// Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_err.clear();
+  return DSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Query rows per sequence at or below which the streaming indexer and the
+// split-row top-k are used (decode and short speculative batches).
+constexpr int kDecodeRows = 8;
+// Budget of materialised prefill scores per chunk of query rows (floats).
+constexpr size_t kScoreBudget = size_t(64) << 20;
+
+dsa_status check_problem(const dsa_problem* p, dsa::Dims& D) {
+  if (!p) return fail(DSA_ERR_INVALID_ARG, "problem pointer is null");
+  if (p->batch < 0 || p->n_q < 0) return fail(DSA_ERR_INVALID_ARG, "batch and n_q must be >= 0");
+  if (p->batch > 65535) return fail(DSA_ERR_INVALID_ARG, "batch %d exceeds 65535", p->batch);
+  if (p->kv_len < 1) return fail(DSA_ERR_INVALID_ARG, "kv_len must be >= 1");
+  if (p->n_q > p->kv_len)
+    return fail(DSA_ERR_INVALID_ARG, "n_q (%d) exceeds kv_len (%d)", p->n_q, p->kv_len);
+  if (p->h_q < 1 || p->h_kv < 1) return fail(DSA_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (p->h_q % p->h_kv != 0)
+    return fail(DSA_ERR_INVALID_ARG, "h_q (%d) is not a multiple of h_kv (%d)", p->h_q, p->h_kv);
+  if (p->top_k < 1) return fail(DSA_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (p->head_dim < 1 || p->idx_dim < 1) return fail(DSA_ERR_INVALID_ARG, "dims must be >= 1");
+  if (!std::isfinite(p->softmax_scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (p->qkv_dtype != DSA_FP32 && p->qkv_dtype != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "qkv_dtype %d is not fp32 (0) or bf16 (1)", p->qkv_dtype);
+  if (p->idx_dtype != DSA_FP32 && p->idx_dtype != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "idx_dtype %d is not fp32 (0) or bf16 (1)", p->idx_dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", p->head_dim);
+  if (p->idx_dim != 16 && p->idx_dim != 32 && p->idx_dim != 64 && p->idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "idx_dim %d not in {16, 32, 64, 128}", p->idx_dim);
+  if (p->h_q / p->h_kv > 256)
+    return fail(DSA_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
+  if ((long long)p->h_q * p->head_dim > (1ll << 20))
+    return fail(DSA_ERR_UNSUPPORTED, "h_q * head_dim too large");
+  D.B = p->batch;
+  D.N = p->n_q;
+  D.L = p->kv_len;
+  D.Hq = p->h_q;
+  D.Hkv = p->h_kv;
+  D.d = p->head_dim;
+  D.didx = p->idx_dim;
+  D.K = p->top_k;
+  D.qkv_bf16 = p->qkv_dtype == DSA_BF16;
+  D.idx_bf16 = p->idx_dtype == DSA_BF16;
+  D.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  return DSA_OK;
+}
+
+bool is_empty(const dsa::Dims& D) { return D.B == 0 || D.N == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout of one call.
+struct Plan {
+  bool decode;     // streaming indexer + split-row top-k
+  int R;           // query rows per chunk
+  size_t scores_off = 0, scores_bytes = 0, ld = 0;
+  size_t tk_off = 0, tk_bytes = 0;      // split top-k scratch
+  size_t idx_off = 0, idx_bytes = 0;    // internal index rows of one chunk
+  size_t part_off = 0, part_bytes = 0;  // attention partials of one chunk
+  int splits_sparse = 1, splits_dense = 1;
+  size_t total = 0;
+};
+
+int prefill_chunk_rows(const dsa::Dims& D) {
+  size_t per_row = (size_t)D.B * D.L;
+  size_t r = std::max<size_t>(64, kScoreBudget / std::max<size_t>(per_row, 1));
+  r = r / 64 * 64;
+  return (int)std::min<size_t>(r, (size_t)D.N);
+}
+
+Plan plan_topk(const dsa::Dims& D) {
+  Plan P;
+  P.decode = D.N <= kDecodeRows;
+  P.R = D.N;
+  if (P.decode) P.tk_bytes = dsa::split_topk_ws_bytes(D, D.N);
+  P.total = align256(P.tk_bytes);
+  return P;
+}
+
+Plan plan_attn(const dsa::Dims& D) {
+  Plan P;
+  P.decode = D.N <= kDecodeRows;
+  P.R = D.N;
+  dsa::attn_pick_splits(D, D.N, P.splits_sparse, P.splits_dense);
+  P.part_bytes = dsa::attn_part_bytes(D, D.N, std::max(P.splits_sparse, P.splits_dense));
+  P.total = align256(P.part_bytes);
+  return P;
+}
+
+Plan plan_fused(const dsa::Dims& D) {
+  Plan P;
+  P.decode = D.N <= kDecodeRows;
+  P.R = P.decode ? D.N : prefill_chunk_rows(D);
+  P.ld = (size_t)D.L;
+  size_t off = 0;
+  P.scores_off = off;
+  P.scores_bytes = (size_t)D.B * P.R * D.L * sizeof(float);
+  off = align256(off + P.scores_bytes);
+  if (P.decode) {
+    P.tk_off = off;
+    P.tk_bytes = dsa::split_topk_ws_bytes(D, P.R);
+    off = align256(off + P.tk_bytes);
+  }
+  P.idx_off = off;
+  P.idx_bytes = (size_t)D.B * P.R * D.K * sizeof(int32_t);
+  off = align256(off + P.idx_bytes);
+  dsa::attn_pick_splits(D, P.R, P.splits_sparse, P.splits_dense);
+  P.part_off = off;
+  P.part_bytes = dsa::attn_part_bytes(D, P.R, std::max(P.splits_sparse, P.splits_dense));
+  off = align256(off + P.part_bytes);
+  P.total = off;
+  return P;
+}
+
+dsa_status check_ws(const Plan& P, void* ws, size_t ws_bytes) {
+  if (P.total == 0) return DSA_OK;
+  if (!ws) return fail(DSA_ERR_WORKSPACE, "workspace is null but %zu bytes are needed", P.total);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < P.total)
+    return fail(DSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, P.total);
+  return DSA_OK;
+}
+
+#define DSA_NEED(ptr, name)                                                       \
+  do {                                                                            \
+    if (!(ptr)) return fail(DSA_ERR_INVALID_ARG, "%s is null", name);             \
+    if (!aligned16(ptr)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+dsa_status hip_status(hipError_t e, const char* where) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+  return ok();
+}
+
+dsa_status check_gate(const float* gate, const float* y2) {
+  if (gate) {
+    if (!aligned16(gate)) return fail(DSA_ERR_INVALID_ARG, "gate is not 16-byte aligned");
+    DSA_NEED(y2, "y2 (required when gate is given)");
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_workspace_size(const dsa_problem* p, size_t* bytes) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is null");
+  if (is_empty(D)) {
+    *bytes = 0;
+    return ok();
+  }
+  const size_t need = std::max({plan_topk(D).total, plan_attn(D).total, plan_fused(D).total});
+  *bytes = need;
+  return ok();
+}
+
+dsa_status dsa_indexer_scores(const dsa_problem* p, const void* q_idx, const void* k_idx,
+                              float* scores, void* stream) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  if (is_empty(D)) return ok();
+  DSA_NEED(q_idx, "q_idx");
+  DSA_NEED(k_idx, "k_idx");
+  DSA_NEED(scores, "scores");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (D.N <= kDecodeRows)
+    e = dsa::launch_indexer_scan(D, q_idx, k_idx, 0, D.N, D.L, scores, (size_t)D.L, true, nullptr, s);
+  else
+    e = dsa::launch_indexer_tiles(D, q_idx, k_idx, 0, D.N, D.L, scores, (size_t)D.L, true, nullptr, s);
+  return hip_status(e, "dsa_indexer_scores");
+}
+
+dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t* topk_idx, void* ws,
+                    size_t ws_bytes, void* stream) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  if (is_empty(D)) return ok();
+  DSA_NEED(scores, "scores");
+  DSA_NEED(topk_idx, "topk_idx");
+  const Plan P = plan_topk(D);
+  if ((st = check_ws(P, ws, ws_bytes)) != DSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (P.decode)
+    e = dsa::launch_topk_split(D, scores, (size_t)D.L, 0, D.N, topk_idx, D.N, 0, nullptr,
+                               (char*)ws + P.tk_off, s);
+  else
+    e = dsa::launch_topk_rows(D, scores, (size_t)D.L, 0, D.N, topk_idx, D.N, 0, nullptr, s);
+  return hip_status(e, "dsa_topk");
+}
+
+dsa_status dsa_sparse_attn(const dsa_problem* p, const void* q, const void* k, const void* v,
+                           const int32_t* topk_idx, const float* gate, const float* y2,
+                           const uint8_t* route, float* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  if (is_empty(D)) return ok();
+  DSA_NEED(q, "q");
+  DSA_NEED(k, "k");
+  DSA_NEED(v, "v");
+  DSA_NEED(topk_idx, "topk_idx");
+  DSA_NEED(out, "out");
+  if ((st = check_gate(gate, y2)) != DSA_OK) return st;
+  const Plan P = plan_attn(D);
+  if ((st = check_ws(P, ws, ws_bytes)) != DSA_OK) return st;
+  dsa::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.topk = topk_idx; a.idx_rows_per_b = D.N; a.idx_n_base = 0;
+  a.gate = gate; a.y2 = y2; a.route = route; a.out = out;
+  a.part = P.part_bytes ? (float*)((char*)ws + P.part_off) : nullptr;
+  a.n0 = 0; a.R = D.N;
+  a.splits_sparse = P.splits_sparse;
+  a.splits_dense = P.splits_dense;
+  return hip_status(dsa::launch_attention(D, a, (hipStream_t)stream), "dsa_sparse_attn");
+}
+
+dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void* k_idx,
+                             const void* q, const void* k, const void* v, const float* gate,
+                             const float* y2, const uint8_t* route, float* out,
+                             int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  if (is_empty(D)) return ok();
+  DSA_NEED(q_idx, "q_idx");
+  DSA_NEED(k_idx, "k_idx");
+  DSA_NEED(q, "q");
+  DSA_NEED(k, "k");
+  DSA_NEED(v, "v");
+  DSA_NEED(out, "out");
+  if (topk_idx_out && !aligned16(topk_idx_out))
+    return fail(DSA_ERR_INVALID_ARG, "topk_idx_out is not 16-byte aligned");
+  if (route && !aligned16(route)) return fail(DSA_ERR_INVALID_ARG, "route is not 16-byte aligned");
+  if ((st = check_gate(gate, y2)) != DSA_OK) return st;
+  const Plan P = plan_fused(D);
+  if ((st = check_ws(P, ws, ws_bytes)) != DSA_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* scores = (float*)(w + P.scores_off);
+  int32_t* idx_chunk = (int32_t*)(w + P.idx_off);
+  float* part = P.part_bytes ? (float*)(w + P.part_off) : nullptr;
+  hipError_t e = hipSuccess;
+  for (int n0 = 0; n0 < D.N && e == hipSuccess; n0 += P.R) {
+    const int R = std::min(P.R, D.N - n0);
+    const int ncols = D.L - D.N + n0 + R;  // keys visible to the last row of the chunk
+    int32_t* idx = topk_idx_out ? topk_idx_out : idx_chunk;
+    const int rows_per_b = topk_idx_out ? D.N : R;
+    const int n_base = topk_idx_out ? 0 : n0;
+    if (P.decode) {
+      e = dsa::launch_indexer_scan(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
+      if (e == hipSuccess)
+        e = dsa::launch_topk_split(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route,
+                                   w + P.tk_off, s);
+    } else {
+      e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
+      if (e == hipSuccess)
+        e = dsa::launch_topk_rows(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route, s);
+    }
+    if (e != hipSuccess) break;
+    dsa::AttnArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.topk = idx; a.idx_rows_per_b = rows_per_b; a.idx_n_base = n_base;
+    a.gate = gate; a.y2 = y2; a.route = route; a.out = out; a.part = part;
+    a.n0 = n0; a.R = R;
+    a.splits_sparse = P.splits_sparse;
+    a.splits_dense = P.splits_dense;
+    e = dsa::launch_attention(D, a, s);
+  }
+  return hip_status(e, "dsa_fused_forward");
+}
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

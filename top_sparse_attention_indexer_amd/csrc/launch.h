@@ -1,0 +1,64 @@
+// Host-side launchers of the libdsa kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct Dims {
+  int B, N, L, Hq, Hkv, d, didx, K;
+  bool qkv_bf16, idx_bf16;
+  float scale;  // resolved softmax scale (> 0)
+};
+
+// ---- indexer ---------------------------------------------------------------
+// Scores of query rows [n0, n0 + R) of every sequence into
+// out[(b * R + r) * ld + j] for j < ncols.  Masked entries (j > p) are written
+// as -inf only if write_masked; tiles that are wholly masked are skipped
+// otherwise.  route (nullable) skips sequences whose heads are all dense.
+hipError_t launch_indexer_tiles(const Dims& D, const void* q_idx, const void* k_idx,
+                                int n0, int R, int ncols, float* out, size_t ld,
+                                bool write_masked, const uint8_t* route, hipStream_t s);
+
+// Streaming variant for few query rows per sequence (R <= 8): one thread per
+// key, every key row read once for all R rows.
+hipError_t launch_indexer_scan(const Dims& D, const void* q_idx, const void* k_idx,
+                               int n0, int R, int ncols, float* out, size_t ld,
+                               bool write_masked, const uint8_t* route, hipStream_t s);
+
+// ---- top-k -----------------------------------------------------------------
+// One workgroup per row: rows r of query rows [n0, n0 + R) of each sequence,
+// scores at scores[(b * R + r) * ld]; index row of query n of sequence b at
+// topk[(b * idx_rows_per_b + n - idx_n_base) * K].
+hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n0, int R,
+                            int32_t* topk, int idx_rows_per_b, int idx_n_base,
+                            const uint8_t* route, hipStream_t s);
+
+// Rows split across workgroups (few, long rows).  Uses `ws` (split_topk_ws_bytes).
+size_t split_topk_ws_bytes(const Dims& D, int R);
+int split_topk_chunk();
+hipError_t launch_topk_split(const Dims& D, const float* scores, size_t ld, int n0, int R,
+                             int32_t* topk, int idx_rows_per_b, int idx_n_base,
+                             const uint8_t* route, void* ws, hipStream_t s);
+
+// ---- attention -------------------------------------------------------------
+struct AttnArgs {
+  const void* q; const void* k; const void* v;
+  const int32_t* topk;      // rows at topk[(b * idx_rows_per_b + n - idx_n_base) * K]
+  int idx_rows_per_b, idx_n_base;
+  const float* gate; const float* y2; const uint8_t* route;
+  float* out;
+  float* part;              // partials for split keys (nullable when splits == 1)
+  int n0, R;                // query rows handled: [n0, n0 + R) of each sequence
+  int splits_sparse, splits_dense;
+};
+size_t attn_part_bytes(const Dims& D, int R, int splits);
+void attn_pick_splits(const Dims& D, int R, int& splits_sparse, int& splits_dense);
+hipError_t launch_attention(const Dims& D, const AttnArgs& a, hipStream_t s);
+
+// ---- misc ------------------------------------------------------------------
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s);
+
+}  // namespace dsa

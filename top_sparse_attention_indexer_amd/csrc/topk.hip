@@ -1,0 +1,337 @@
+// Exact top-K per query row with ties to the lower position.
+//
+// Selection rule of the page "超大规模MoE架构中稀疏注意力机制的演进与实践"
+// (§二.1: keep the K = 2048 best-scoring past positions whatever the context
+// length) and of "混合注意力架构演进：从线性注意力到稀疏门控的技术权衡" (§三,
+// an index array of shape [L, top_k]); rows with at most K visible keys keep
+// all of them.
+//
+// Method: radix select on the order-preserving 32-bit key of each float score
+// in three digit passes (11, 11, 10 bits) with LDS histograms, which yields the
+// exact K-th key T and the number kk of keys equal to T that are still needed.
+// An ordered compaction (wave ballots + popcounts, blocks scanned in position
+// order) then writes every key > T and the first kk keys == T, ascending.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kShift[3] = {21, 10, 0};
+constexpr int kBins[3] = {2048, 2048, 1024};
+
+__device__ __forceinline__ bool row_has_sparse(const uint8_t* route, int b, int Hq) {
+  if (!route) return true;
+  for (int h = 0; h < Hq; ++h)
+    if (route[(size_t)b * Hq + h]) return true;
+  return false;
+}
+
+// Finds the bin t holding the kk-th largest element of hist[0..nb) (counting
+// from the top) and the count of elements in bins above t.  Every thread of
+// the block must call it; the result lands in res[0] (bin) and res[1] (count
+// above).  nb must be a multiple of NT.
+template <int NT>
+__device__ void pick_bin(const uint32_t* hist, int nb, uint32_t kk, uint32_t* scratch,
+                         uint32_t* res) {
+  const int per = nb / NT;
+  const int base = threadIdx.x * per;
+  uint32_t mine = 0;
+  for (int i = 0; i < per; ++i) mine += hist[base + i];
+  uint32_t total;
+  const uint32_t pre = block_excl_scan<NT>(mine, scratch, total);
+  uint32_t running = total - pre - mine;  // elements in bins above this thread's bins
+  for (int i = per - 1; i >= 0; --i) {
+    const uint32_t c = hist[base + i];
+    if (running < kk && running + c >= kk) {
+      res[0] = (uint32_t)(base + i);
+      res[1] = running;
+    }
+    running += c;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- one row per workgroup
+constexpr int RT = 1024;
+
+__global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ scores, size_t ld,
+                                                  int N, int L, int K, int n0, int R,
+                                                  int32_t* __restrict__ topk, int idx_rows_per_b,
+                                                  int idx_n_base, const uint8_t* __restrict__ route,
+                                                  int Hq) {
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int n = n0 + r;
+  int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
+  const int vis = L - N + n + 1;
+  if (!row_has_sparse(route, b, Hq)) {
+    for (int i = threadIdx.x; i < K; i += RT) o[i] = -1;
+    return;
+  }
+  if (vis <= K) {
+    for (int i = threadIdx.x; i < K; i += RT) o[i] = (i < vis) ? i : -1;
+    return;
+  }
+  const float* row = scores + ((size_t)b * R + r) * ld;
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scratch[RT / DSA_WAVE + 1];
+  __shared__ uint32_t res[2];
+
+  uint32_t prefix = 0, mask = 0, kk = (uint32_t)K;
+  for (int lv = 0; lv < 3; ++lv) {
+    const int shift = kShift[lv], nb = kBins[lv];
+    for (int i = threadIdx.x; i < nb; i += RT) hist[i] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < vis; j += RT) {
+      const uint32_t u = radix_key(row[j]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    pick_bin<RT>(hist, nb, kk, scratch, res);
+    const uint32_t t = res[0], above = res[1];
+    prefix |= t << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    kk -= above;
+    __syncthreads();
+  }
+
+  const uint32_t T = prefix;
+  uint32_t base_sel = 0, base_tie = 0;
+  for (int start = 0; start < vis; start += RT) {
+    const int j = start + threadIdx.x;
+    const uint32_t u = (j < vis) ? radix_key(row[j]) : 0u;
+    const bool gt = (j < vis) && u > T;
+    const bool eq = (j < vis) && u == T;
+    uint32_t tie_tot, sel_tot;
+    const uint32_t tie_rank = block_rank<RT>(eq, scratch, tie_tot);
+    const bool sel = gt || (eq && base_tie + tie_rank < kk);
+    const uint32_t pos = block_rank<RT>(sel, scratch, sel_tot);
+    if (sel && base_sel + pos < (uint32_t)K) o[base_sel + pos] = j;
+    base_tie += tie_tot;
+    base_sel += sel_tot;
+  }
+}
+
+// ---------------------------------------------------------------- rows split over workgroups
+constexpr int ST = 256;      // threads per workgroup
+constexpr int SCH = 8192;    // scores per chunk
+constexpr int kHistWords = 2048 + 2048 + 1024;
+
+struct SplitWs {
+  uint32_t* hist;   // [rows][5120]
+  uint32_t* cnt;    // [rows][nchunks][2]  (count > T, count == T)
+  uint32_t* state;  // [rows][2]           (T, kk)
+  int nchunks;
+};
+
+__device__ __forceinline__ uint32_t* level_hist(uint32_t* h, int lv) {
+  return h + (lv == 0 ? 0 : (lv == 1 ? 2048 : 4096));
+}
+
+// Rebuilds (prefix, mask, kk) after `levels` digit passes from the global
+// histograms of one row.  Every thread of the block must call it.
+__device__ void split_state(const uint32_t* ghist, int levels, int K, uint32_t* lhist,
+                            uint32_t* scratch, uint32_t* res, uint32_t& prefix, uint32_t& mask,
+                            uint32_t& kk) {
+  prefix = 0;
+  mask = 0;
+  kk = (uint32_t)K;
+  for (int lv = 0; lv < levels; ++lv) {
+    const int nb = kBins[lv];
+    const uint32_t* g = ghist + (lv == 0 ? 0 : (lv == 1 ? 2048 : 4096));
+    for (int i = threadIdx.x; i < nb; i += ST) lhist[i] = g[i];
+    __syncthreads();
+    pick_bin<ST>(lhist, nb, kk, scratch, res);
+    prefix |= res[0] << kShift[lv];
+    mask |= (uint32_t)(nb - 1) << kShift[lv];
+    kk -= res[1];
+    __syncthreads();
+  }
+}
+
+template <int LV>
+__global__ __launch_bounds__(ST) void k_split_hist(const float* __restrict__ scores, size_t ld,
+                                                   int N, int L, int K, int n0, int R,
+                                                   SplitWs ws, const uint8_t* __restrict__ route,
+                                                   int Hq) {
+  const int c = blockIdx.x, row = blockIdx.y;  // row = b * R + r
+  const int b = row / R, r = row - b * R;
+  const int vis = L - N + n0 + r + 1;
+  if (vis <= K || !row_has_sparse(route, b, Hq)) return;
+  const int j0 = c * SCH, j1 = min(vis, j0 + SCH);
+  if (j0 >= j1) return;
+  __shared__ uint32_t lhist[2048];
+  __shared__ uint32_t scratch[ST / DSA_WAVE + 1];
+  __shared__ uint32_t res[2];
+  uint32_t* gh = ws.hist + (size_t)row * kHistWords;
+  uint32_t prefix, mask, kk;
+  split_state(gh, LV, K, lhist, scratch, res, prefix, mask, kk);
+  const int nb = kBins[LV], shift = kShift[LV];
+  for (int i = threadIdx.x; i < nb; i += ST) lhist[i] = 0;
+  __syncthreads();
+  const float* srow = scores + (size_t)row * ld;
+  for (int j = j0 + threadIdx.x; j < j1; j += ST) {
+    const uint32_t u = radix_key(srow[j]);
+    if ((u & mask) == prefix) atomicAdd(&lhist[(u >> shift) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  uint32_t* g = level_hist(gh, LV);
+  for (int i = threadIdx.x; i < nb; i += ST) {
+    const uint32_t v = lhist[i];
+    if (v) atomicAdd(&g[i], v);
+  }
+}
+
+__global__ __launch_bounds__(ST) void k_split_count(const float* __restrict__ scores, size_t ld,
+                                                    int N, int L, int K, int n0, int R,
+                                                    SplitWs ws, const uint8_t* __restrict__ route,
+                                                    int Hq) {
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int b = row / R, r = row - b * R;
+  const int vis = L - N + n0 + r + 1;
+  if (vis <= K || !row_has_sparse(route, b, Hq)) return;
+  const int j0 = c * SCH, j1 = min(vis, j0 + SCH);
+  __shared__ uint32_t lhist[2048];
+  __shared__ uint32_t scratch[ST / DSA_WAVE + 1];
+  __shared__ uint32_t res[2];
+  uint32_t prefix, mask, kk;
+  split_state(ws.hist + (size_t)row * kHistWords, 3, K, lhist, scratch, res, prefix, mask, kk);
+  const uint32_t T = prefix;
+  uint32_t gt = 0, eq = 0;
+  const float* srow = scores + (size_t)row * ld;
+  for (int j = j0 + threadIdx.x; j < j1; j += ST) {
+    const uint32_t u = radix_key(srow[j]);
+    gt += (u > T);
+    eq += (u == T);
+  }
+  uint32_t tgt, teq;
+  block_excl_scan<ST>(gt, scratch, tgt);
+  block_excl_scan<ST>(eq, scratch, teq);
+  if (threadIdx.x == 0) {
+    uint32_t* cc = ws.cnt + ((size_t)row * ws.nchunks + c) * 2;
+    cc[0] = tgt;
+    cc[1] = teq;
+    if (c == 0) {
+      ws.state[(size_t)row * 2 + 0] = T;
+      ws.state[(size_t)row * 2 + 1] = kk;
+    }
+  }
+}
+
+__global__ __launch_bounds__(ST) void k_split_compact(const float* __restrict__ scores, size_t ld,
+                                                      int N, int L, int K, int n0, int R,
+                                                      SplitWs ws, int32_t* __restrict__ topk,
+                                                      int idx_rows_per_b, int idx_n_base,
+                                                      const uint8_t* __restrict__ route, int Hq) {
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int b = row / R, r = row - b * R;
+  const int n = n0 + r;
+  const int vis = L - N + n + 1;
+  int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
+  if (!row_has_sparse(route, b, Hq)) {
+    if (c == 0)
+      for (int i = threadIdx.x; i < K; i += ST) o[i] = -1;
+    return;
+  }
+  if (vis <= K) {
+    const int i0 = c * SCH, i1 = min(vis, i0 + SCH);
+    for (int i = i0 + threadIdx.x; i < i1; i += ST) o[i] = i;
+    if (c == 0)
+      for (int i = vis + threadIdx.x; i < K; i += ST) o[i] = -1;
+    return;
+  }
+  const int j0 = c * SCH, j1 = min(vis, j0 + SCH);
+  if (j0 >= j1) return;
+  __shared__ uint32_t scratch[ST / DSA_WAVE + 1];
+  __shared__ uint32_t bases[2];
+  const uint32_t T = ws.state[(size_t)row * 2 + 0];
+  const uint32_t kk = ws.state[(size_t)row * 2 + 1];
+  if (threadIdx.x == 0) {
+    uint32_t sel_base = 0, tie_base = 0;
+    const uint32_t* cc = ws.cnt + (size_t)row * ws.nchunks * 2;
+    for (int i = 0; i < c; ++i) {
+      const uint32_t g = cc[2 * i], e = cc[2 * i + 1];
+      const uint32_t take = (kk > tie_base) ? min(e, kk - tie_base) : 0u;
+      sel_base += g + take;
+      tie_base += e;
+    }
+    bases[0] = sel_base;
+    bases[1] = tie_base;
+  }
+  __syncthreads();
+  uint32_t base_sel = bases[0], base_tie = bases[1];
+  const float* srow = scores + (size_t)row * ld;
+  for (int start = j0; start < j1; start += ST) {
+    const int j = start + threadIdx.x;
+    const uint32_t u = (j < j1) ? radix_key(srow[j]) : 0u;
+    const bool gt = (j < j1) && u > T;
+    const bool eq = (j < j1) && u == T;
+    uint32_t tie_tot, sel_tot;
+    const uint32_t tie_rank = block_rank<ST>(eq, scratch, tie_tot);
+    const bool sel = gt || (eq && base_tie + tie_rank < kk);
+    const uint32_t pos = block_rank<ST>(sel, scratch, sel_tot);
+    if (sel && base_sel + pos < (uint32_t)K) o[base_sel + pos] = j;
+    base_tie += tie_tot;
+    base_sel += sel_tot;
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n0, int R,
+                            int32_t* topk, int idx_rows_per_b, int idx_n_base,
+                            const uint8_t* route, hipStream_t s) {
+  if (D.B == 0 || R == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_topk_rows, dim3(R, D.B), dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R,
+                     topk, idx_rows_per_b, idx_n_base, route, D.Hq);
+  return hipGetLastError();
+}
+
+int split_topk_chunk() { return SCH; }
+
+size_t split_topk_ws_bytes(const Dims& D, int R) {
+  const size_t rows = (size_t)D.B * R;
+  const size_t nch = ((size_t)D.L + SCH - 1) / SCH;
+  return rows * (kHistWords + nch * 2 + 2) * sizeof(uint32_t);
+}
+
+hipError_t launch_topk_split(const Dims& D, const float* scores, size_t ld, int n0, int R,
+                             int32_t* topk, int idx_rows_per_b, int idx_n_base,
+                             const uint8_t* route, void* wsp, hipStream_t s) {
+  if (D.B == 0 || R == 0) return hipSuccess;
+  const int rows = D.B * R;
+  SplitWs ws;
+  ws.nchunks = (D.L + SCH - 1) / SCH;
+  ws.hist = (uint32_t*)wsp;
+  ws.cnt = ws.hist + (size_t)rows * kHistWords;
+  ws.state = ws.cnt + (size_t)rows * ws.nchunks * 2;
+  hipError_t e = launch_fill_u32(ws.hist, (size_t)rows * kHistWords, 0u, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid(ws.nchunks, rows);
+  hipLaunchKernelGGL(k_split_hist<0>, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
+                     route, D.Hq);
+  hipLaunchKernelGGL(k_split_hist<1>, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
+                     route, D.Hq);
+  hipLaunchKernelGGL(k_split_hist<2>, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
+                     route, D.Hq);
+  hipLaunchKernelGGL(k_split_count, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
+                     route, D.Hq);
+  hipLaunchKernelGGL(k_split_compact, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
+                     topk, idx_rows_per_b, idx_n_base, route, D.Hq);
+  return hipGetLastError();
+}
+
+}  // namespace dsa
