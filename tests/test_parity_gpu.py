@@ -150,6 +150,10 @@ EDGE = [
     ("mixed_route", _w(2, 70, 300, 8, 2, 128, 64, 32, route_p=0.5, seed=5)),
     ("fp32_d64", _w(1, 130, 130, 6, 3, 64, 64, 17, dt="fp32")),
     ("mqa_decode_many_heads", _w(1, 1, 50000, 64, 1, 128, 64, 2048)),
+    ("spec_decode_4_rows", _w(2, 4, 30001, 8, 2, 128, 64, 1000)),
+    ("decode_fp32_idx32", _w(3, 2, 9000, 4, 2, 64, 32, 333, dt="fp32")),
+    ("decode_mixed_route", _w(4, 1, 12000, 8, 2, 128, 64, 500, route_p=0.5, seed=3)),
+    ("decode_4_rows_long_ctx", _w(2, 4, 600000, 4, 1, 64, 64, 2048)),
 ]
 
 

@@ -1,0 +1,864 @@
+// Decode path in one cooperative launch: indexer scan, exact top-K, ordered
+// index rows, gathered attention and gate, for few query rows per sequence.
+//
+// Steps of the gated sparse forward on the page "超大规模MoE架构中稀疏注意力机制的
+// 演进与实践" (§二.1 indexer + top-K, §二.2 no rotary term, §四.1 gather ->
+// attention -> gate) for the case where every sequence has a few new tokens
+// and a long cache.  Blockwise selection without a global score matrix, in
+// the spirit of the page "大模型推理架构演进：从稀疏注意力到隐式专家路由"
+// §2.2-§2.3, with scores kept in LDS.
+//
+// Every workgroup owns one chunk of one sequence's keys (its "unit") for the
+// whole launch.  The grid is sized to what the device holds at once (from the
+// occupancy query) and phases are separated by a two-level grid barrier whose
+// wait is bounded.
+//   P1  stream k_idx once: scores of the chunk's keys for all N rows into LDS;
+//       first-digit (top 11 key bits) histogram per row -> global.
+//   P2  bin t0 holding the K-th key; per chunk the count of keys above t0;
+//       keys in t0 appended to the row's candidates, their second digit
+//       (next 11 bits) histogrammed -> global.
+//   P3  each unit resolves its row's exact K-th key T (t1 from the second
+//       histogram, last digit and tie cut P* from the few candidates sharing
+//       the top 22 bits) and writes its chunk's selected positions, in order,
+//       at its prefix offset -> ascending index rows.
+//   P4  attention items (row, KV head, key split, head chunk): each wave
+//       scores 64 keys (lane = key), online softmax, PV with lane = value
+//       slice; the last split of a (row, KV head, head chunk) merges the
+//       partials and applies the gate.
+#include <map>
+#include <mutex>
+
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int DT = 256;        // threads per workgroup
+constexpr int DSC = 8192;      // LDS score capacity per workgroup (floats)
+constexpr int DMAXCH = 2048;   // max chunks per sequence
+constexpr int kMaxGrid = 4096;  // largest grid the control block is sized for
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  const void* q_idx; const void* k_idx; const void* q; const void* k; const void* v;
+  const float* gate; const float* y2; const uint8_t* route; float* out; int32_t* list;
+  uint32_t* ctl;     // barrier counters, error flag          (zeroed before launch)
+  uint32_t* hist0;   // [rows][2048] first-digit histogram   (zeroed before launch)
+  uint32_t* hist1;   // [rows][2048] second-digit histogram  (zeroed before launch)
+  uint32_t* cand_n;  // [rows] candidate counts              (zeroed before launch)
+  uint32_t* ticket;  // [rows][Hkv][nhc] finished splits     (zeroed before launch)
+  uint32_t* cnt;     // [rows][nch] keys above the first-digit bin, per chunk
+  uint64_t* cand;    // [rows][cand_cap]     key << 32 | position
+  float* part;       // [rows][Hq][S][HD+2]
+  int B, N, L, Hq, Hkv, K, CH, nch, S, nhc, cand_cap;
+  float scale_log2;
+};
+
+__device__ __forceinline__ bool seq_sparse(const uint8_t* route, int b, int Hq) {
+  if (!route) return true;
+  for (int h = 0; h < Hq; ++h)
+    if (route[(size_t)b * Hq + h]) return true;
+  return false;
+}
+
+// Cross-workgroup data is written with device-scope atomic stores and read
+// with device-scope atomic loads: both bypass the per-XCD L2 copies, so no
+// L2 writeback / invalidate (the expensive part of a device-scope fence) is
+// needed around the grid barrier.  Counters and histograms use atomic RMWs.
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_devf(float* p, float v) { st_dev((uint32_t*)p, __float_as_uint(v)); }
+__device__ __forceinline__ float ld_devf(const float* p) { return __uint_as_float(ld_dev((const uint32_t*)p)); }
+
+constexpr int kBarGroup = 16;   // workgroups per first-level barrier counter
+// ctl words: [0] second-level counter, [1] error flag, [2] release generation,
+// [64 + 64 * g] first-level counter of group g (one cache line apart).
+size_t ctl_words(int grid) { return 64 + 64 * (size_t)((grid + kBarGroup - 1) / kBarGroup); }
+
+// Two-level grid barrier with a bounded wait.  Each thread first waits for its
+// own outstanding memory operations, so every store issued before the barrier
+// has completed when the workgroup arrives.  Returns false (and raises the
+// error flag) if the grid did not arrive in time or another workgroup gave up.
+__device__ bool grid_sync(uint32_t* ctl, uint32_t phase, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int G = gridDim.x;
+    const int ngroups = (G + kBarGroup - 1) / kBarGroup;
+    const int g = blockIdx.x / kBarGroup;
+    const uint32_t gsize = (uint32_t)min(kBarGroup, G - g * kBarGroup);
+    const uint32_t old = atomicAdd(&ctl[64 + 64 * g], 1u);
+    if (old + 1 == phase * gsize) {
+      const uint32_t o2 = atomicAdd(&ctl[0], 1u);
+      if (o2 + 1 == phase * (uint32_t)ngroups) atomicAdd(&ctl[2], 1u);
+    }
+    int good = 1;
+    uint32_t spins = 0;
+    while (ld_dev(&ctl[2]) < phase) {
+      if (ld_dev(&ctl[1]) != 0u) {
+        good = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > (1u << 24)) {
+        atomicOr(&ctl[1], 1u);
+        good = 0;
+        break;
+      }
+    }
+    *flag = good;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// kk-th largest (from the top) over hist[0..nb): bin and count above it.
+__device__ void pick_top(const uint32_t* hist, int nb, uint32_t kk, uint32_t* scratch,
+                         uint32_t* res) {
+  const int per = nb / DT;
+  const int base = threadIdx.x * per;
+  uint32_t mine = 0;
+  for (int i = 0; i < per; ++i) mine += hist[base + i];
+  uint32_t total;
+  const uint32_t pre = block_excl_scan<DT>(mine, scratch, total);
+  uint32_t running = total - pre - mine;
+  for (int i = per - 1; i >= 0; --i) {
+    const uint32_t c = hist[base + i];
+    if (running < kk && running + c >= kk) {
+      res[0] = (uint32_t)(base + i);
+      res[1] = running;
+    }
+    running += c;
+  }
+  __syncthreads();
+}
+
+// kk-th smallest (from the bottom) over hist[0..nb): bin and count below it.
+__device__ void pick_low(const uint32_t* hist, int nb, uint32_t kk, uint32_t* scratch,
+                         uint32_t* res) {
+  const int per = nb / DT;
+  const int base = threadIdx.x * per;
+  uint32_t mine = 0;
+  for (int i = 0; i < per; ++i) mine += hist[base + i];
+  uint32_t total;
+  uint32_t running = block_excl_scan<DT>(mine, scratch, total);
+  for (int i = 0; i < per; ++i) {
+    const uint32_t c = hist[base + i];
+    if (running < kk && running + c >= kk) {
+      res[0] = (uint32_t)(base + i);
+      res[1] = running;
+    }
+    running += c;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* scratch) {
+  uint32_t total;
+  block_excl_scan<DT>(x, scratch, total);
+  return total;
+}
+
+// 16-byte load widened to float: 8 bf16 or 4 fp32 elements.
+__device__ __forceinline__ void ld16(const bf16_bits* p, float* o) { ld8(p, o); }
+__device__ __forceinline__ void ld16(const float* p, float* o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
+__device__ __forceinline__ uint4 raw16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void widen(const uint4& u, float* o, const bf16_bits*) {
+  o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+  o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+  o[4] = __uint_as_float(u.z << 16); o[5] = __uint_as_float(u.z & 0xffff0000u);
+  o[6] = __uint_as_float(u.w << 16); o[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+__device__ __forceinline__ void widen(const uint4& u, float* o, const float*) {
+  o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
+  o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
+}
+
+// One attention pass of an item: heads hsel[0..nh) of KV head g, keys given
+// by the index-row segment [e0, e1) (sparse) or positions [e0, e1) (dense).
+// Each wave takes 64 keys at a time: scores with lane = key, online softmax
+// per wave, PV with lane = (key slot, 16-byte slice of the value row).  The
+// four waves are merged through LDS; one partial (max, sum, acc) per head is
+// written for split s.  Loads are issued in batches of 8 per lane.
+template <typename TQ, int HD, int HCT>
+__device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
+                       int e0, int e1, const int* hsel, int nh, float* lds) {
+  constexpr int EPV = 16 / (int)sizeof(TQ);   // elements per 16-byte load
+  constexpr int LPR = HD / EPV;               // lanes per value row
+  constexpr int KPI = 64 / LPR;               // value rows per load instruction
+  constexpr int NKL = HD / EPV;               // 16-byte loads per key row
+  constexpr int BATCH = 8;
+  const TQ* K = (const TQ*)a.k;
+  const TQ* V = (const TQ*)a.v;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int p = a.L - a.N + n;
+  float* qs = lds;                     // [HCT][HD]
+  float* wb = lds + HCT * HD;          // [4][HCT][HD]
+  float* wml = wb + 4 * HCT * HD;      // [4][HCT][2]
+  for (int e = threadIdx.x; e < HCT * HD; e += DT) {
+    const int hh = e / HD, c = e - hh * HD;
+    float x = 0.f;
+    if (hh < nh) x = ld_f((const TQ*)a.q, (((size_t)b * a.N + n) * a.Hq + hsel[hh]) * HD + c) *
+                     a.scale_log2;
+    qs[e] = x;
+  }
+  __syncthreads();
+  float m_w[HCT], l_w[HCT], acc[HCT][EPV];
+#pragma unroll
+  for (int h = 0; h < HCT; ++h) {
+    m_w[h] = -INFINITY;
+    l_w[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) acc[h][i] = 0.f;
+  }
+  const uint32_t* lrow = (const uint32_t*)a.list + (size_t)row * a.K;
+  const int ks = lane / LPR, dc = lane % LPR;
+  for (int t0 = e0 + w * 64; t0 < e1; t0 += 4 * 64) {
+    const int e = t0 + lane;
+    int j = -1;
+    if (e < e1) {
+      j = dense ? e : (int)ld_dev(lrow + e);
+      if (j < 0 || j > p) j = -1;
+    }
+    float sc[HCT];
+#pragma unroll
+    for (int h = 0; h < HCT; ++h) sc[h] = 0.f;
+    const TQ* kr = K + (((size_t)b * a.L + (j < 0 ? 0 : j)) * a.Hkv + g) * HD;
+#pragma unroll 1
+    for (int c0 = 0; c0 < NKL; c0 += BATCH) {
+      uint4 raw[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i)
+        raw[i] = (j >= 0) ? raw16(kr + (c0 + i) * EPV) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        float kv[EPV];
+        widen(raw[i], kv, (const TQ*)nullptr);
+#pragma unroll
+        for (int h = 0; h < HCT; ++h) {
+          float t = sc[h];
+#pragma unroll
+          for (int x = 0; x < EPV; ++x) t = fmaf(qs[h * HD + (c0 + i) * EPV + x], kv[x], t);
+          sc[h] = t;
+        }
+      }
+    }
+    float pr[HCT];
+#pragma unroll
+    for (int h = 0; h < HCT; ++h) {
+      const float sv = (j >= 0 && h < nh) ? sc[h] : -INFINITY;
+      const float mt = wave_max(sv);
+      const float mnew = fmaxf(m_w[h], mt);
+      float alpha = 1.f, pv = 0.f;
+      if (mnew != -INFINITY) {
+        alpha = exp2f(m_w[h] - mnew);
+        pv = exp2f(sv - mnew);
+      }
+      l_w[h] = l_w[h] * alpha + wave_sum(pv);
+      m_w[h] = mnew;
+      pr[h] = pv;
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) acc[h][i] *= alpha;
+    }
+    // PV: lane = (key slot ks, dims dc*EPV ..)
+#pragma unroll 1
+    for (int t = 0; t < 64; t += KPI * BATCH) {
+      uint4 raw[BATCH];
+      int jv[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        jv[i] = __shfl(j, t + i * KPI + ks, 64);
+        raw[i] = (jv[i] >= 0)
+                     ? raw16(V + (((size_t)b * a.L + jv[i]) * a.Hkv + g) * HD + dc * EPV)
+                     : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        float vv[EPV];
+        widen(raw[i], vv, (const TQ*)nullptr);
+#pragma unroll
+        for (int h = 0; h < HCT; ++h) {
+          const float pv = __shfl(pr[h], t + i * KPI + ks, 64);
+#pragma unroll
+          for (int x = 0; x < EPV; ++x) acc[h][x] = fmaf(pv, vv[x], acc[h][x]);
+        }
+      }
+    }
+  }
+  // reduce over key slots
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < HCT; ++h)
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) acc[h][i] += __shfl_xor(acc[h][i], o, 64);
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < HCT; ++h)
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) wb[(w * HCT + h) * HD + lane * EPV + i] = acc[h][i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < HCT; ++h) {
+      wml[(w * HCT + h) * 2 + 0] = m_w[h];
+      wml[(w * HCT + h) * 2 + 1] = l_w[h];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nh * HD; e += DT) {
+    const int hh = e / HD, c = e - hh * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, wml[(ww * HCT + hh) * 2]);
+    float l = 0.f, s_acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = wml[(ww * HCT + hh) * 2];
+        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        l = fmaf(f, wml[(ww * HCT + hh) * 2 + 1], l);
+        s_acc = fmaf(f, wb[(ww * HCT + hh) * HD + c], s_acc);
+      }
+    }
+    float* pp = a.part + (((size_t)row * a.Hq + hsel[hh]) * a.S + s) * (HD + 2);
+    st_devf(pp + 2 + c, s_acc);
+    if (c == 0) {
+      st_devf(pp + 0, M);
+      st_devf(pp + 1, l);
+    }
+  }
+  __syncthreads();
+}
+
+template <typename TI, int DIDX, typename TQ, int HD, int HCT>
+__global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
+  __shared__ float lds[10240];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scratch[DT / DSA_WAVE + 1];
+  __shared__ uint32_t res[4];
+  __shared__ int flag;
+  __shared__ int hsel[2][HCT];
+  __shared__ int nsel[2];
+  __shared__ uint32_t t0s[4], kk0s[4];
+
+  const int G = gridDim.x;
+  const int u = blockIdx.x;
+  const bool has_unit = u < a.B * a.nch;
+  const int b = has_unit ? u / a.nch : 0;
+  const int c = has_unit ? u - b * a.nch : 0;
+  const int j0 = c * a.CH;
+  const int clen = has_unit ? min(a.CH, a.L - j0) : 0;
+  const bool sp = has_unit && seq_sparse(a.route, b, a.Hq);
+  const int N = a.N, K = a.K;
+
+  // ---------------------------------------------------------------- P1 scan
+  if (sp) {
+    constexpr int EPL = 16 / (int)sizeof(TI);
+    constexpr int LPK = DIDX / EPL;
+    constexpr int KPW = 64 / LPK;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int sub = lane % LPK, kin = lane / LPK;
+    const TI* qi = (const TI*)a.q_idx;
+    const TI* ki = (const TI*)a.k_idx;
+    float qv[4][EPL];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        qv[n][e] = (n < N) ? ld_f(qi, ((size_t)b * N + n) * DIDX + sub * EPL + e) : 0.f;
+    constexpr int U = 8;
+    for (int base = w * KPW; base < clen; base += 4 * KPW * U) {
+      uint4 raw[U];
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const int jj = base + kin + uu * 4 * KPW;
+        raw[uu] = (jj < clen) ? raw16(ki + ((size_t)b * a.L + j0 + jj) * DIDX + sub * EPL)
+                              : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const int jj = base + kin + uu * 4 * KPW;
+        float kv[EPL];
+        widen(raw[uu], kv, (const TI*)nullptr);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          if (n >= N) break;
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s = fmaf(qv[n][e], kv[e], s);
+#pragma unroll
+          for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+          if (sub == 0 && jj < clen) lds[n * a.CH + jj] = s;
+        }
+      }
+    }
+    __syncthreads();
+    for (int n = 0; n < N; ++n) {
+      const int vis = a.L - N + n + 1;
+      if (vis <= K) continue;
+      const int lim = min(clen, vis - j0);
+      for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+      __syncthreads();
+      for (int jj = threadIdx.x; jj < lim; jj += DT)
+        atomicAdd(&hist[radix_key(lds[n * a.CH + jj]) >> 21], 1u);
+      __syncthreads();
+      uint32_t* gh = a.hist0 + ((size_t)b * N + n) * 2048;
+      for (int i = threadIdx.x; i < 2048; i += DT)
+        if (hist[i]) atomicAdd(&gh[i], hist[i]);
+      __syncthreads();
+    }
+  }
+  if (!grid_sync(a.ctl, 1u, &flag)) return;
+
+  // ---------------------------------------------------------------- P2 candidates
+  // t0 = bin of the K-th key; keys above it are counted per chunk, keys in it
+  // become candidates and feed the second-digit histogram.
+  if (sp) {
+    for (int n = 0; n < N; ++n) {
+      const int vis = a.L - N + n + 1;
+      if (vis <= K) continue;
+      const int row = b * N + n;
+      const uint32_t* gh = a.hist0 + (size_t)row * 2048;
+#pragma unroll
+      for (int i = 0; i < 2048 / DT; ++i) hist[threadIdx.x + i * DT] = ld_dev(gh + threadIdx.x + i * DT);
+      __syncthreads();
+      pick_top(hist, 2048, (uint32_t)K, scratch, res);
+      const uint32_t t0 = res[0];
+      if (threadIdx.x == 0) {
+        t0s[n] = t0;
+        kk0s[n] = (uint32_t)K - res[1];
+      }
+      const int lim = min(clen, vis - j0);
+      uint32_t above = 0, ncand = 0;
+      for (int jj = threadIdx.x; jj < lim; jj += DT) {
+        const uint32_t bin = radix_key(lds[n * a.CH + jj]) >> 21;
+        above += bin > t0;
+        ncand += bin == t0;
+      }
+      uint32_t tot_c;
+      const uint32_t pre = block_excl_scan<DT>(ncand, scratch, tot_c);
+      const uint32_t tot_a = block_sum(above, scratch);
+      if (threadIdx.x == 0) {
+        res[2] = tot_c ? atomicAdd(&a.cand_n[row], tot_c) : 0u;
+        st_dev(&a.cnt[(size_t)row * a.nch + c], tot_a);
+      }
+      for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+      __syncthreads();
+      uint32_t slot = res[2] + pre;
+      uint64_t* cr = (uint64_t*)a.cand + (size_t)row * a.cand_cap;
+      for (int jj = threadIdx.x; jj < lim; jj += DT) {
+        const uint32_t key = radix_key(lds[n * a.CH + jj]);
+        if ((key >> 21) == t0) {
+          if (slot < (uint32_t)a.cand_cap)
+            st_dev64(cr + slot, ((uint64_t)key << 32) | (uint32_t)(j0 + jj));
+          ++slot;
+          atomicAdd(&hist[(key >> 10) & 2047u], 1u);
+        }
+      }
+      __syncthreads();
+      uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
+      for (int i = threadIdx.x; i < 2048; i += DT)
+        if (hist[i]) atomicAdd(&gh1[i], hist[i]);
+      __syncthreads();
+    }
+  }
+  if (!grid_sync(a.ctl, 2u, &flag)) return;
+
+  // ---------------------------------------------------------------- P3 select + ordered rows
+  // Every unit resolves its row's exact threshold itself (no further
+  // barrier): t1 from the second-digit histogram, then the few candidates
+  // sharing the top two digits give the exact K-th key T and the position cut
+  // P* for ties.  The unit's offset in the index row is the number of
+  // selected keys in the chunks before it.
+  if (has_unit) {
+    for (int n = 0; n < N; ++n) {
+      const int row = b * N + n;
+      const int vis = a.L - N + n + 1;
+      uint32_t* lr = (uint32_t*)a.list + (size_t)row * K;
+      if (!sp) {
+        if (c == 0)
+          for (int i = threadIdx.x; i < K; i += DT) st_dev(lr + i, 0xffffffffu);
+        continue;
+      }
+      if (vis <= K) {
+        const int lim = min(clen, vis - j0);
+        for (int jj = threadIdx.x; jj < lim; jj += DT) st_dev(lr + j0 + jj, (uint32_t)(j0 + jj));
+        if (c == 0)
+          for (int i = vis + threadIdx.x; i < K; i += DT) st_dev(lr + i, 0xffffffffu);
+        continue;
+      }
+      const uint32_t t0 = t0s[n];
+      uint32_t kk = kk0s[n];
+      const uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
+#pragma unroll
+      for (int i = 0; i < 2048 / DT; ++i) hist[threadIdx.x + i * DT] = ld_dev(gh1 + threadIdx.x + i * DT);
+      __syncthreads();
+      pick_top(hist, 2048, kk, scratch, res);
+      const uint32_t t1 = res[0];
+      kk -= res[1];
+      const uint32_t m = hist[t1];              // candidates sharing digits t0, t1
+      const int nc = (int)min(ld_dev(&a.cand_n[row]), (uint32_t)a.cand_cap);
+      const uint64_t* crg = (const uint64_t*)a.cand + (size_t)row * a.cand_cap;
+      const uint32_t pfx = (t0 << 11) | t1;      // top 22 bits of T
+      const int cap_lds = (10240 - ((N * a.CH + 1) & ~1)) / 2;
+      uint64_t* cl = (uint64_t*)(lds + ((N * a.CH + 1) & ~1));
+      const bool in_lds = m <= (uint32_t)cap_lds;
+      if (threadIdx.x == 0) res[3] = 0;
+      __syncthreads();
+      // one pass over the row's candidates: selected-for-sure ones before this
+      // chunk, and the ones sharing the top two digits (kept in LDS)
+      uint32_t before = 0;
+      for (int i0 = 0; i0 < nc; i0 += DT * 4) {
+        uint64_t v4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = i0 + x * DT + threadIdx.x;
+          v4[x] = (i < nc) ? ld_dev64(crg + i) : 0ull;
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = i0 + x * DT + threadIdx.x;
+          if (i >= nc) continue;
+          const uint32_t key = (uint32_t)(v4[x] >> 32), pos = (uint32_t)v4[x];
+          const uint32_t top = key >> 10;
+          if (top > pfx && pos < (uint32_t)j0) ++before;
+          if (top == pfx && in_lds) cl[atomicAdd(&res[3], 1u)] = v4[x];
+        }
+      }
+      __syncthreads();
+      auto cand = [&](uint32_t i) -> uint64_t { return in_lds ? cl[i] : ld_dev64(crg + i); };
+      const uint32_t nl = in_lds ? m : (uint32_t)nc;   // entries to scan for the last digit
+      // digit 3: key bits 9..0 among the candidates with prefix pfx
+      for (int i = threadIdx.x; i < 1024; i += DT) hist[i] = 0;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+        const uint32_t key = (uint32_t)(cand(i) >> 32);
+        if ((key >> 10) == pfx) atomicAdd(&hist[key & 1023u], 1u);
+      }
+      __syncthreads();
+      pick_top(hist, 1024, kk, scratch, res);
+      const uint32_t t2 = res[0];
+      kk -= res[1];
+      const uint32_t ties = hist[t2];
+      const uint32_t T = (pfx << 10) | t2;
+      __syncthreads();
+      uint32_t pstar = 0x7fffffffu;
+      if (kk < ties) {
+        // kk-th smallest position among the keys equal to T
+        uint32_t pprefix = 0, pmask = 0;
+        const int pshift[3] = {20, 10, 0};
+        const int pbins[3] = {2048, 1024, 1024};
+        for (int lv = 0; lv < 3; ++lv) {
+          const int nb = pbins[lv], sh = pshift[lv];
+          for (int i = threadIdx.x; i < nb; i += DT) hist[i] = 0;
+          __syncthreads();
+          for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+            const uint64_t cd = cand(i);
+            const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
+            if (key == T && (pos & pmask) == pprefix) atomicAdd(&hist[(pos >> sh) & (nb - 1)], 1u);
+          }
+          __syncthreads();
+          pick_low(hist, nb, kk, scratch, res);
+          pprefix |= res[0] << sh;
+          pmask |= (uint32_t)(nb - 1) << sh;
+          kk -= res[1];
+          __syncthreads();
+        }
+        pstar = pprefix;
+      }
+      // selected candidates with the top-two-digit prefix before this chunk
+      for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+        const uint64_t cd = cand(i);
+        const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
+        if ((key >> 10) == pfx && pos < (uint32_t)j0 && (key > T || (key == T && pos <= pstar)))
+          ++before;
+      }
+      // keys in bins above t0 before this chunk
+      const uint32_t* cc = a.cnt + (size_t)row * a.nch;
+      for (int i = threadIdx.x; i < c; i += DT) before += ld_dev(cc + i);
+      uint32_t base = block_sum(before, scratch);
+      const int lim = min(clen, vis - j0);
+      for (int s0 = 0; s0 < lim; s0 += DT) {
+        const int jj = s0 + threadIdx.x;
+        bool sel = false;
+        if (jj < lim) {
+          const uint32_t key = radix_key(lds[n * a.CH + jj]);
+          sel = key > T || (key == T && (uint32_t)(j0 + jj) <= pstar);
+        }
+        uint32_t tot;
+        const uint32_t rk = block_rank<DT>(sel, scratch, tot);
+        if (sel && base + rk < (uint32_t)K) st_dev(lr + base + rk, (uint32_t)(j0 + jj));
+        base += tot;
+      }
+    }
+  }
+  if (!grid_sync(a.ctl, 3u, &flag)) return;
+
+  // ---------------------------------------------------------------- P4 attention + merge
+  // Items (row, KV head, key split, head chunk).  The last split of a
+  // (row, KV head, head chunk) to finish merges the partials and applies the
+  // gate (ticket counter), so no further grid barrier is needed.
+  {
+    const int G_heads = a.Hq / a.Hkv;
+    const int items = a.B * N * a.Hkv * a.S * a.nhc;
+    const int per_s = ((K + a.S - 1) / a.S + 63) / 64 * 64;
+    const int per_d = ((a.L + a.S - 1) / a.S + 63) / 64 * 64;
+    for (int it = blockIdx.x; it < items; it += G) {
+      // split index is the fastest-varying so that the splits of one
+      // (row, KV head, head chunk) run side by side
+      int rem = it;
+      const int s = rem % a.S; rem /= a.S;
+      const int hci = rem % a.nhc; rem /= a.nhc;
+      const int g = rem % a.Hkv; rem /= a.Hkv;
+      const int row = rem;
+      const int rb = row / N, rn = row - rb * N;
+      if (threadIdx.x == 0) {
+        int ns = 0, nd = 0;
+        for (int i = hci * HCT; i < min(G_heads, hci * HCT + HCT); ++i) {
+          const int h = g * G_heads + i;
+          const bool sparse = a.route ? (a.route[(size_t)rb * a.Hq + h] != 0) : true;
+          if (sparse) hsel[0][ns++] = h;
+          else hsel[1][nd++] = h;
+        }
+        nsel[0] = ns;
+        nsel[1] = nd;
+      }
+      __syncthreads();
+      const int ns = nsel[0], nd = nsel[1];
+      const int vis = a.L - N + rn + 1;
+      if (ns > 0) {
+        const int e0 = s * per_s, e1 = min(K, e0 + per_s);
+        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds);
+      }
+      if (nd > 0) {
+        const int e0 = s * per_d, e1 = min(vis, e0 + per_d);
+        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds);
+      }
+      // ticket: the last split of this (row, g, hci) merges
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t t = atomicAdd(&a.ticket[((size_t)row * a.Hkv + g) * a.nhc + hci], 1u);
+        res[0] = (t + 1 == (uint32_t)a.S) ? 1u : 0u;
+      }
+      __syncthreads();
+      if (res[0]) {
+        const int nh = ns + nd;
+        for (int e = threadIdx.x; e < nh * HD; e += DT) {
+          const int hh = e / HD, cth = e - hh * HD;
+          const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
+          const float* pp = a.part + ((size_t)row * a.Hq + h) * a.S * (HD + 2);
+          float M = -INFINITY;
+          for (int s2 = 0; s2 < a.S; ++s2) M = fmaxf(M, ld_devf(pp + s2 * (HD + 2)));
+          float val = 0.f;
+          if (M != -INFINITY) {
+            float l = 0.f, acc = 0.f;
+            for (int s2 = 0; s2 < a.S; ++s2) {
+              const float ms = ld_devf(pp + s2 * (HD + 2));
+              const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+              l = fmaf(f, ld_devf(pp + s2 * (HD + 2) + 1), l);
+              acc = fmaf(f, ld_devf(pp + s2 * (HD + 2) + 2 + cth), acc);
+            }
+            val = (l > 0.f) ? acc / l : 0.f;
+          }
+          const size_t orow = (size_t)row * a.Hq + h;
+          if (a.gate) {
+            const float gg = a.gate[orow];
+            val = fmaf(gg, val, (1.f - gg) * a.y2[orow * HD + cth]);
+          }
+          a.out[orow * HD + cth] = val;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <typename TI, int DIDX, typename TQ, int HD>
+const void* decode_kernel(int G) {
+  if (G <= 4) return reinterpret_cast<const void*>(&k_decode<TI, DIDX, TQ, HD, 4>);
+  return reinterpret_cast<const void*>(&k_decode<TI, DIDX, TQ, HD, 8>);
+}
+
+template <typename TI, typename TQ, int HD>
+const void* pick_didx(int didx, int G) {
+  switch (didx) {
+    case 16: return decode_kernel<TI, 16, TQ, HD>(G);
+    case 32: return decode_kernel<TI, 32, TQ, HD>(G);
+    case 64: return decode_kernel<TI, 64, TQ, HD>(G);
+    default: return decode_kernel<TI, 128, TQ, HD>(G);
+  }
+}
+
+const void* select_kernel(const Dims& D) {
+  const int G = D.Hq / D.Hkv;
+  if (D.idx_bf16) {
+    if (D.qkv_bf16) return D.d == 128 ? pick_didx<bf16_bits, bf16_bits, 128>(D.didx, G)
+                                      : pick_didx<bf16_bits, bf16_bits, 64>(D.didx, G);
+    return D.d == 128 ? pick_didx<bf16_bits, float, 128>(D.didx, G)
+                      : pick_didx<bf16_bits, float, 64>(D.didx, G);
+  }
+  if (D.qkv_bf16) return D.d == 128 ? pick_didx<float, bf16_bits, 128>(D.didx, G)
+                                    : pick_didx<float, bf16_bits, 64>(D.didx, G);
+  return D.d == 128 ? pick_didx<float, float, 128>(D.didx, G)
+                    : pick_didx<float, float, 64>(D.didx, G);
+}
+
+int coresident_blocks(const void* fn) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({fn, dev});
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, DT, 0) != hipSuccess) return 0;
+  per = std::min(per, 2);
+  cache[{fn, dev}] = cus * per;
+  return cus * per;
+}
+
+}  // namespace
+
+bool decode_plan(const Dims& D, int grid, DecodePlan& P) {
+  if (D.N < 1 || D.N > 4 || grid <= 0 || grid > kMaxGrid) return false;
+  const int rows = D.B * D.N;
+  if (rows > grid) return false;
+  // smallest chunk (multiple of 256) with one unit per workgroup
+  long long ch = ((long long)D.B * D.L + grid - 1) / grid;
+  ch = std::max<long long>(256, (ch + 255) / 256 * 256);
+  while ((long long)D.B * ((D.L + ch - 1) / ch) > grid) ch += 256;
+  if (ch * D.N > DSC) return false;
+  const int nch = (int)((D.L + ch - 1) / ch);
+  if (nch > DMAXCH) return false;
+  P.grid = grid;
+  P.CH = (int)ch;
+  P.nch = nch;
+  const int G = D.Hq / D.Hkv;
+  const int hct = G <= 4 ? 4 : 8;
+  P.nhc = (G + hct - 1) / hct;
+  const long long base_items = (long long)rows * D.Hkv * P.nhc;
+  long long S = (D.K + 255) / 256;
+  const long long smax = (D.K + 63) / 64;
+  while (S < smax && base_items * S * 2 <= grid) S *= 2;
+  P.S = (int)std::min(S, smax);
+  P.cand_cap = D.L;
+  return true;
+}
+
+int decode_grid(const Dims& D) { return coresident_blocks(select_kernel(D)); }
+
+size_t decode_ws_bound(const Dims& D) {
+  DecodePlan P;
+  P.nch = (int)std::min<long long>(DMAXCH, ((long long)D.L + 255) / 256);
+  P.S = (D.K + 63) / 64;
+  P.cand_cap = D.L;
+  return decode_ws_bytes(D, P);
+}
+
+// Workspace layout (all offsets 256-byte aligned): the zeroed block (control
+// words, both digit histograms, candidate counts, tickets), then per-chunk
+// counts, candidates and attention partials.
+struct DecodeLayout {
+  size_t ctl, hist0, hist1, cand_n, ticket, zero_end, cnt, cand, part, total;
+};
+
+DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
+  const size_t rows = (size_t)D.B * D.N;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  DecodeLayout Lo;
+  size_t off = 0;
+  Lo.ctl = off;    off = al(off + ctl_words(kMaxGrid) * 4);
+  Lo.hist0 = off;  off = al(off + rows * 2048 * 4);
+  Lo.hist1 = off;  off = al(off + rows * 2048 * 4);
+  Lo.cand_n = off; off = al(off + rows * 4);
+  Lo.ticket = off; off = al(off + rows * D.Hkv * (size_t)P.nhc * 4);
+  Lo.zero_end = off;
+  Lo.cnt = off;    off = al(off + rows * (size_t)P.nch * 4);
+  Lo.cand = off;   off = al(off + rows * (size_t)P.cand_cap * 8);
+  Lo.part = off;   off = al(off + rows * D.Hq * (size_t)P.S * (D.d + 2) * 4);
+  Lo.total = off;
+  return Lo;
+}
+
+size_t decode_ws_bytes(const Dims& D, const DecodePlan& P) { return decode_layout(D, P).total; }
+
+// Launches of this kernel are ordered across streams: all of its workgroups
+// must be resident at once, so two of them must not share the GPU.
+struct StreamOrder {
+  std::mutex mu;
+  hipStream_t last = nullptr;
+  bool have_last = false;
+  hipEvent_t done = nullptr;
+};
+
+StreamOrder& stream_order(int dev) {
+  static StreamOrder orders[64];
+  return orders[dev & 63];
+}
+
+hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, const void* k_idx,
+                         const void* q, const void* k, const void* v, const float* gate,
+                         const float* y2, const uint8_t* route, float* out, int32_t* list,
+                         void* ws, hipStream_t s) {
+  char* w = (char*)ws;
+  const DecodeLayout Lo = decode_layout(D, P);
+  DecodeArgs a{};
+  a.q_idx = q_idx; a.k_idx = k_idx; a.q = q; a.k = k; a.v = v;
+  a.gate = gate; a.y2 = y2; a.route = route; a.out = out; a.list = list;
+  a.ctl = (uint32_t*)(w + Lo.ctl);
+  a.hist0 = (uint32_t*)(w + Lo.hist0);
+  a.hist1 = (uint32_t*)(w + Lo.hist1);
+  a.cand_n = (uint32_t*)(w + Lo.cand_n);
+  a.ticket = (uint32_t*)(w + Lo.ticket);
+  a.cnt = (uint32_t*)(w + Lo.cnt);
+  a.cand = (uint64_t*)(w + Lo.cand);
+  a.part = (float*)(w + Lo.part);
+  a.B = D.B; a.N = D.N; a.L = D.L; a.Hq = D.Hq; a.Hkv = D.Hkv; a.K = D.K;
+  a.CH = P.CH; a.nch = P.nch; a.S = P.S; a.nhc = P.nhc; a.cand_cap = P.cand_cap;
+  a.scale_log2 = D.scale * kLog2e;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  StreamOrder& so = stream_order(dev);
+  std::lock_guard<std::mutex> lock(so.mu);
+  if (!so.done) {
+    e = hipEventCreateWithFlags(&so.done, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  if (so.have_last && so.last != s) {
+    e = hipStreamWaitEvent(s, so.done, 0);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_fill_u32((uint32_t*)w, Lo.zero_end / 4, 0u, s);
+  if (e != hipSuccess) return e;
+  void* args[] = {&a};
+  e = hipLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(so.done, s);
+  so.last = s;
+  so.have_last = true;
+  return e;
+}
+
+}  // namespace dsa

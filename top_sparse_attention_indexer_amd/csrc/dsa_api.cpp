@@ -83,6 +83,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout of one call.
 struct Plan {
+  bool fused_decode = false;  // one cooperative launch (few rows, scores in LDS)
+  dsa::DecodePlan dp;
+  size_t dec_off = 0, dec_bytes = 0;
   bool decode;     // streaming indexer + split-row top-k
   int R;           // query rows per chunk
   size_t scores_off = 0, scores_bytes = 0, ld = 0;
@@ -119,8 +122,29 @@ Plan plan_attn(const dsa::Dims& D) {
   return P;
 }
 
-Plan plan_fused(const dsa::Dims& D) {
+// Few query rows: the single-launch decode kernel when its grid and LDS limits
+// allow (needs a device to size the co-resident grid).
+bool plan_fused_decode(const dsa::Dims& D, Plan& P) {
+  if (D.N > 4) return false;
+  const int grid = dsa::decode_grid(D);
+  if (grid <= 0 || !dsa::decode_plan(D, grid, P.dp)) return false;
+  P.fused_decode = true;
+  P.decode = true;
+  P.R = D.N;
+  size_t off = 0;
+  P.dec_off = off;
+  P.dec_bytes = dsa::decode_ws_bytes(D, P.dp);
+  off = align256(off + P.dec_bytes);
+  P.idx_off = off;
+  P.idx_bytes = (size_t)D.B * D.N * D.K * sizeof(int32_t);
+  off = align256(off + P.idx_bytes);
+  P.total = off;
+  return true;
+}
+
+Plan plan_fused(const dsa::Dims& D, bool allow_single_launch = true) {
   Plan P;
+  if (allow_single_launch && plan_fused_decode(D, P)) return P;
   P.decode = D.N <= kDecodeRows;
   P.R = P.decode ? D.N : prefill_chunk_rows(D);
   P.ld = (size_t)D.L;
@@ -185,7 +209,10 @@ dsa_status dsa_workspace_size(const dsa_problem* p, size_t* bytes) {
     *bytes = 0;
     return ok();
   }
-  const size_t need = std::max({plan_topk(D).total, plan_attn(D).total, plan_fused(D).total});
+  size_t need = std::max({plan_topk(D).total, plan_attn(D).total, plan_fused(D, false).total});
+  if (D.N <= 4)  // the single-launch decode plan, for any grid size
+    need = std::max(need, align256(dsa::decode_ws_bound(D)) +
+                              align256((size_t)D.B * D.N * D.K * sizeof(int32_t)));
   *bytes = need;
   return ok();
 }
@@ -278,6 +305,12 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
 
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
+  if (P.fused_decode) {
+    int32_t* list = topk_idx_out ? topk_idx_out : (int32_t*)(w + P.idx_off);
+    return hip_status(dsa::launch_decode(D, P.dp, q_idx, k_idx, q, k, v, gate, y2, route, out,
+                                         list, w + P.dec_off, s),
+                      "dsa_fused_forward");
+  }
   float* scores = (float*)(w + P.scores_off);
   int32_t* idx_chunk = (int32_t*)(w + P.idx_off);
   float* part = P.part_bytes ? (float*)(w + P.part_off) : nullptr;

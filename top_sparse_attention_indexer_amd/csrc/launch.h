@@ -58,6 +58,27 @@ size_t attn_part_bytes(const Dims& D, int R, int splits);
 void attn_pick_splits(const Dims& D, int R, int& splits_sparse, int& splits_dense);
 hipError_t launch_attention(const Dims& D, const AttnArgs& a, hipStream_t s);
 
+// ---- fused decode (one cooperative launch) ----------------------------------
+struct DecodePlan {
+  int grid = 0;      // co-resident workgroups
+  int CH = 0;        // keys per chunk (one chunk per workgroup)
+  int nch = 0;       // chunks per sequence
+  int S = 1;         // attention key splits
+  int nhc = 1;       // head chunks per KV head
+  int cand_cap = 0;  // candidate slots per row
+};
+// Co-resident grid for the decode kernel of these dims on the current device
+// (0 if it cannot be determined, e.g. without a GPU).
+int decode_grid(const Dims& D);
+bool decode_plan(const Dims& D, int grid, DecodePlan& P);
+size_t decode_ws_bytes(const Dims& D, const DecodePlan& P);
+// Upper bound of decode_ws_bytes over every grid size.
+size_t decode_ws_bound(const Dims& D);
+hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, const void* k_idx,
+                         const void* q, const void* k, const void* v, const float* gate,
+                         const float* y2, const uint8_t* route, float* out, int32_t* list,
+                         void* ws, hipStream_t s);
+
 // ---- misc ------------------------------------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s);
 
