@@ -234,6 +234,19 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
       j = dense ? e : (int)ld_dev(lrow + e);
       if (j < 0 || j > p) j = -1;
     }
+    // bf16 value rows are fetched before the scores are computed (their
+    // addresses are already known), so their latency overlaps the key work
+    constexpr bool PREF = sizeof(TQ) == 2 && HCT <= 4;
+    constexpr int NVL = 64 / KPI;               // value loads per lane per 64 keys
+    uint4 vraw[PREF ? NVL : 1];
+    if constexpr (PREF) {
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) {
+        const int jv = __shfl(j, i * KPI + ks, 64);
+        vraw[i] = (jv >= 0) ? raw16(V + (((size_t)b * a.L + jv) * a.Hkv + g) * HD + dc * EPV)
+                            : make_uint4(0, 0, 0, 0);
+      }
+    }
     float sc[HCT];
 #pragma unroll
     for (int h = 0; h < HCT; ++h) sc[h] = 0.f;
@@ -275,26 +288,38 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
       for (int i = 0; i < EPV; ++i) acc[h][i] *= alpha;
     }
     // PV: lane = (key slot ks, dims dc*EPV ..)
-#pragma unroll 1
-    for (int t = 0; t < 64; t += KPI * BATCH) {
-      uint4 raw[BATCH];
-      int jv[BATCH];
+    if constexpr (PREF) {
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        jv[i] = __shfl(j, t + i * KPI + ks, 64);
-        raw[i] = (jv[i] >= 0)
-                     ? raw16(V + (((size_t)b * a.L + jv[i]) * a.Hkv + g) * HD + dc * EPV)
-                     : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
+      for (int i = 0; i < NVL; ++i) {
         float vv[EPV];
-        widen(raw[i], vv, (const TQ*)nullptr);
+        widen(vraw[i], vv, (const TQ*)nullptr);
 #pragma unroll
         for (int h = 0; h < HCT; ++h) {
-          const float pv = __shfl(pr[h], t + i * KPI + ks, 64);
+          const float pv = __shfl(pr[h], i * KPI + ks, 64);
 #pragma unroll
           for (int x = 0; x < EPV; ++x) acc[h][x] = fmaf(pv, vv[x], acc[h][x]);
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int t = 0; t < 64; t += KPI * BATCH) {
+        uint4 raw[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const int jv = __shfl(j, t + i * KPI + ks, 64);
+          raw[i] = (jv >= 0) ? raw16(V + (((size_t)b * a.L + jv) * a.Hkv + g) * HD + dc * EPV)
+                             : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          float vv[EPV];
+          widen(raw[i], vv, (const TQ*)nullptr);
+#pragma unroll
+          for (int h = 0; h < HCT; ++h) {
+            const float pv = __shfl(pr[h], t + i * KPI + ks, 64);
+#pragma unroll
+            for (int x = 0; x < EPV; ++x) acc[h][x] = fmaf(pv, vv[x], acc[h][x]);
+          }
         }
       }
     }
@@ -658,24 +683,49 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       }
       __syncthreads();
       if (res[0]) {
+        // stage every split's (max, sum) in LDS, then the weighted sum of the
+        // accumulators with the loads of 8 splits in flight per thread
         const int nh = ns + nd;
+        const int S = a.S;
+        float* mls = lds;                  // [nh][S][2]
+        float* wts = mls + nh * S * 2;     // [nh][S]
+        float* lsum = wts + nh * S;        // [nh]
+        for (int e = threadIdx.x; e < nh * S; e += DT) {
+          const int hh = e / S, s2 = e - hh * S;
+          const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
+          const float* pp = a.part + (((size_t)row * a.Hq + h) * S + s2) * (HD + 2);
+          mls[2 * e] = ld_devf(pp);
+          mls[2 * e + 1] = ld_devf(pp + 1);
+        }
+        __syncthreads();
+        for (int hh = threadIdx.x; hh < nh; hh += DT) {
+          float M = -INFINITY;
+          for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, mls[2 * (hh * S + s2)]);
+          float l = 0.f;
+          for (int s2 = 0; s2 < S; ++s2) {
+            const float ms = mls[2 * (hh * S + s2)];
+            const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+            wts[hh * S + s2] = f;
+            l = fmaf(f, mls[2 * (hh * S + s2) + 1], l);
+          }
+          lsum[hh] = l;
+        }
+        __syncthreads();
         for (int e = threadIdx.x; e < nh * HD; e += DT) {
           const int hh = e / HD, cth = e - hh * HD;
           const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
-          const float* pp = a.part + ((size_t)row * a.Hq + h) * a.S * (HD + 2);
-          float M = -INFINITY;
-          for (int s2 = 0; s2 < a.S; ++s2) M = fmaxf(M, ld_devf(pp + s2 * (HD + 2)));
-          float val = 0.f;
-          if (M != -INFINITY) {
-            float l = 0.f, acc = 0.f;
-            for (int s2 = 0; s2 < a.S; ++s2) {
-              const float ms = ld_devf(pp + s2 * (HD + 2));
-              const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-              l = fmaf(f, ld_devf(pp + s2 * (HD + 2) + 1), l);
-              acc = fmaf(f, ld_devf(pp + s2 * (HD + 2) + 2 + cth), acc);
-            }
-            val = (l > 0.f) ? acc / l : 0.f;
+          const float* pp = a.part + ((size_t)row * a.Hq + h) * S * (HD + 2) + 2 + cth;
+          float acc = 0.f;
+          for (int s0 = 0; s0 < S; s0 += 8) {
+            float v8[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v8[x] = (s0 + x < S) ? ld_devf(pp + (s0 + x) * (HD + 2)) : 0.f;
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+              if (s0 + x < S) acc = fmaf(wts[hh * S + s0 + x], v8[x], acc);
           }
+          const float l = lsum[hh];
+          float val = (l > 0.f) ? acc / l : 0.f;
           const size_t orow = (size_t)row * a.Hq + h;
           if (a.gate) {
             const float gg = a.gate[orow];
