@@ -1,0 +1,405 @@
+// Attention with bf16 MFMA for prefill-shaped calls: both routes of the
+// per-head route in one launch.
+//
+// Sparse heads: softmax(q k^T * scale) v over the selected rows of each query
+// token ("混合注意力架构演进：从线性注意力到稀疏门控的技术权衡" §三; steps 3-4 of
+// the gated forward on "超大规模MoE架构中稀疏注意力机制的演进与实践" §四.1).
+// Dense heads: full causal attention ("Advanced Attention Mechanisms" article
+// §2.1) with the running max / running sum over key tiles of its §3.2.  The
+// page "Elastic Attention：动态路由优化大模型长文本处理" §3.1 puts both kinds of
+// head in one fused op with load balancing; here the grid is one list of
+// work items, dense query tiles first (longest first), then sparse tokens.
+//
+// Per 32-key step and wave (all math in fp32 accumulators):
+//   S^T [16 keys x 16 cols] = K_tile [16 x d] . Q^T [d x 16]   (two halves)
+//     K rows go straight from memory into the MFMA A operand; the 16 columns
+//     are 16 query rows of one head (dense) or the heads of one KV head
+//     (sparse).  The d axis is visited in a permuted order so that each lane
+//     reads 64 contiguous bytes of a key row; Q^T uses the same order.
+//   online softmax per column, in registers (a lane owns one column);
+//   O^T [16 dims x 16 cols] += V^T [16 dims x 32 keys] . P^T [32 keys x 16]
+//     P^T is the MFMA B operand directly from registers (keys 4q..4q+3 of
+//     the first half and 16+4q.. of the second half for lane quad q); V^T is
+//     read from a row-major LDS tile with the transposing LDS load, which
+//     hands lane i of a 16-lane group element i%4 of the 8-byte chunks read
+//     by lanes 4k + i/4.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int MT = 256;          // threads (4 waves)
+constexpr int VSTR = 288;        // LDS row stride of a 32 x d value tile (bytes)
+constexpr int KSTR = 272;        // LDS row stride of a 32 x d key tile (bytes)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* p) {
+  uint4 u;
+  u.x = bf16_rne(p[0]) | (bf16_rne(p[1]) << 16);
+  u.y = bf16_rne(p[2]) | (bf16_rne(p[3]) << 16);
+  u.z = bf16_rne(p[4]) | (bf16_rne(p[5]) << 16);
+  u.w = bf16_rne(p[6]) | (bf16_rne(p[7]) << 16);
+  return as_bf16x8(u);
+}
+
+__device__ __forceinline__ uint2 lds_tr(const char* lds_base, int byte_off) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) char*)lds_base + byte_off));
+  uint2 r;
+  __builtin_memcpy(&r, &v, 8);
+  return r;
+}
+
+struct MfmaArgs {
+  const bf16_bits* q; const bf16_bits* k; const bf16_bits* v;
+  const int32_t* topk; int idx_rows_per_b, idx_n_base;
+  const float* gate; const float* y2; const uint8_t* route;
+  float* out;
+  int B, N, L, Hq, Hkv, K;
+  int n0, R;          // query rows [n0, n0 + R) of each sequence
+  int qtiles;         // dense query tiles of 64 rows per (b, h)
+  float scale_log2;
+};
+
+// Shared per-step core: given this wave's two 16-key halves (A operands for
+// S^T already loaded), the 32 x d value tile in LDS, update the running
+// state of the lane's column.
+template <int HD>
+struct ColState {
+  float m, l;
+  f32x4 o[HD / 16];
+};
+
+template <int HD>
+__device__ __forceinline__ void step_core(const uint4 (&ka)[2][HD / 32], const bf16x8 (&qb)[HD / 32],
+                                          const bool (&kvalid)[2][4], const char* vtile,
+                                          float scale_log2, ColState<HD>& st) {
+  constexpr int T = HD / 32;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, i = lane & 15;
+  float s[8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[u][t]), qb[t], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[u * 4 + r] = kvalid[u][r] ? acc[r] * scale_log2 : -INFINITY;
+  }
+  float mt = s[0];
+#pragma unroll
+  for (int x = 1; x < 8; ++x) mt = fmaxf(mt, s[x]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mnew = fmaxf(st.m, mt);
+  float alpha = 1.f;
+  float p[8];
+  if (mnew == -INFINITY) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) p[x] = 0.f;
+  } else {
+    alpha = exp2f(st.m - mnew);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) p[x] = exp2f(s[x] - mnew);
+  }
+  float ps = 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) ps += p[x];
+  st.l = st.l * alpha + ps;  // this lane's keys only; summed over quads at the end
+  st.m = mnew;
+  const bf16x8 pb = pack8(p);
+  // value tile rows: first half keys 4q+k, second half 16+4q+k; this lane
+  // (4k + c within its 16-lane group) points at row 4q + i/4, dims 4*(i%4)
+  const int row0 = 4 * q + (i >> 2);
+  const int colb = (i & 3) * 8;  // bytes
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) {
+    const uint2 lo = lds_tr(vtile, row0 * VSTR + dt * 32 + colb);
+    const uint2 hi = lds_tr(vtile, (16 + row0) * VSTR + dt * 32 + colb);
+    uint4 u;
+    u.x = lo.x; u.y = lo.y; u.z = hi.x; u.w = hi.y;
+    f32x4 o = st.o[dt];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] *= alpha;
+    st.o[dt] = mfma16(as_bf16x8(u), pb, o);
+  }
+}
+
+// Final normalisation, gate and store of one column (lane owns column i; the
+// four quads hold dims 16*dt + 4q + r).
+template <int HD>
+__device__ __forceinline__ void finish_col(ColState<HD>& st, const MfmaArgs& a, size_t orow,
+                                           bool write) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  float l = st.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!write) return;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  const float g = a.gate ? a.gate[orow] : 1.f;
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) {
+    const int d0 = dt * 16 + 4 * q;
+    float4 r;
+    float* rv = &r.x;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      float val = (l > 0.f) ? st.o[dt][x] * inv : 0.f;
+      if (a.gate) val = fmaf(g, val, (1.f - g) * a.y2[orow * HD + d0 + x]);
+      rv[x] = val;
+    }
+    *reinterpret_cast<float4*>(a.out + orow * HD + d0) = r;
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(MT) void k_attn_mfma(MfmaArgs a) {
+  constexpr int T = HD / 32;
+  // sparse: per-wave value tile + the token's index row; dense: shared tiles
+  __shared__ __attribute__((aligned(16))) char vt[4][32 * VSTR];
+  __shared__ __attribute__((aligned(16))) char kt[32 * KSTR];
+  __shared__ int ilist[2048];
+  __shared__ int s_nd, s_lastv;
+  __shared__ int s_pair;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, i = lane & 15;
+  const int Gh = a.Hq / a.Hkv;
+
+  // number of dense (b, h) pairs
+  if (threadIdx.x == 0) {
+    int nd = 0;
+    if (a.route)
+      for (int x = 0; x < a.B * a.Hq; ++x) nd += a.route[x] == 0;
+    s_nd = nd;
+  }
+  __syncthreads();
+  const int nd = s_nd;
+  const long long n_dense_items = (long long)nd * a.qtiles;
+  const long long item = blockIdx.x;
+
+  if (item < n_dense_items) {
+    // ------------------------------------------------------------ dense query tile
+    const int tile = a.qtiles - 1 - (int)(item / nd);   // longest tiles first
+    const int d_idx = (int)(item % nd);
+    if (threadIdx.x == 0) {
+      int c = -1, x = 0;
+      for (; x < a.B * a.Hq; ++x)
+        if (a.route[x] == 0 && ++c == d_idx) break;
+      s_pair = x;
+    }
+    __syncthreads();
+    const int pair = s_pair;
+    const int b = pair / a.Hq, h = pair - b * a.Hq, g = h / Gh;
+    const int rbase = tile * 64;                // local row within [0, R)
+    const int myrow = rbase + w * 16 + i;       // this lane's column = query row
+    const bool rvalid = myrow < a.R;
+    const int n = a.n0 + myrow;
+    const int p = a.L - a.N + n;                // last visible key of the row
+    const int rlast = min(a.R - 1, rbase + 63);
+    const int pmax = a.L - a.N + a.n0 + rlast;
+    const int pmin_wave = a.L - a.N + a.n0 + rbase + w * 16;
+    // Q^T operand (dims in the permuted order q*32 + t*8)
+    bf16x8 qb[T];
+    {
+      const bf16_bits* qr = a.q + (((size_t)b * a.N + (rvalid ? n : a.n0)) * a.Hq + h) * HD;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        uint4 u = rvalid ? *reinterpret_cast<const uint4*>(qr + q * (HD / 4) + t * 8)
+                         : make_uint4(0, 0, 0, 0);
+        qb[t] = as_bf16x8(u);
+      }
+    }
+    ColState<HD> st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
+    const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
+    const size_t rstride = (size_t)a.Hkv * HD;   // elements between key rows
+    char* vtile = vt[0];
+    for (int j0 = 0; j0 <= pmax; j0 += 32) {
+      // cooperative load of the K tile (row-major, 256 B rows for d = 128) and
+      // the V tile (288 B stride) into LDS
+      constexpr int CPR = HD / 8;                // 16-byte chunks per row
+      for (int cidx = threadIdx.x; cidx < 32 * CPR; cidx += MT) {
+        const int r = cidx / CPR, cc = cidx - r * CPR;
+        const int j = j0 + r;
+        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        if (j <= pmax) {
+          kv = *reinterpret_cast<const uint4*>(kbase + (size_t)j * rstride + cc * 8);
+          vv = *reinterpret_cast<const uint4*>(vbase + (size_t)j * rstride + cc * 8);
+        }
+        *reinterpret_cast<uint4*>(kt + r * KSTR + cc * 16) = kv;
+        *reinterpret_cast<uint4*>(vtile + r * VSTR + cc * 16) = vv;
+      }
+      __syncthreads();
+      if (j0 <= pmin_wave + 15) {   // some row of this wave sees a key of the tile
+        uint4 ka[2][T];
+        bool kval[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            ka[u][t] = *reinterpret_cast<const uint4*>(kt + (u * 16 + i) * KSTR +
+                                                        (q * (HD / 4) + t * 8) * 2);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) kval[u][r] = rvalid && (j0 + u * 16 + 4 * q + r) <= p;
+        }
+        // A operand rows are the keys: lane (q, i) supplies key i of the half;
+        // the output row index (keys 4q + r) belongs to the column lane.
+        step_core<HD>(ka, qb, kval, vtile, a.scale_log2, st);
+      }
+      __syncthreads();
+    }
+    const size_t orow = ((size_t)b * a.N + n) * a.Hq + h;
+    finish_col<HD>(st, a, orow, rvalid);
+    return;
+  }
+
+  // -------------------------------------------------------------- sparse token
+  const long long sidx = item - n_dense_items;
+  if (sidx >= (long long)a.B * a.R) return;
+  const int b = (int)(sidx / a.R), r_loc = (int)(sidx - (long long)b * a.R);
+  const int n = a.n0 + r_loc;
+  const int p = a.L - a.N + n;
+  // index row into LDS; the last valid entry bounds the loop
+  const int32_t* irow = a.topk + ((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.K;
+  if (threadIdx.x == 0) s_lastv = -1;
+  __syncthreads();
+  int lastv = -1;
+  const int kpad = (a.K + 31) / 32 * 32;
+  for (int e = threadIdx.x; e < kpad; e += MT) {
+    int j = (e < a.K) ? irow[e] : -1;
+    if (j < 0 || j > p) j = -1;
+    ilist[e] = j;
+    if (j >= 0) lastv = e;
+  }
+  if (lastv >= 0) atomicMax(&s_lastv, lastv);
+  __syncthreads();
+  const int nsteps = (s_lastv + 32) / 32;
+  char* vtile = vt[w];
+  const size_t rstride = (size_t)a.Hkv * HD;
+  // (KV head, 16-head chunk) pairs spread over the four waves
+  const int nhc = (Gh + 15) / 16;
+  for (int pi = w; pi < a.Hkv * nhc; pi += 4) {
+    const int g = pi / nhc;
+    {
+      const int hc = (pi - g * nhc) * 16;
+      int myh = -1, cnt = 0;
+      for (int x = hc; x < min(Gh, hc + 16); ++x) {
+        const int h = g * Gh + x;
+        const bool sp = a.route ? a.route[(size_t)b * a.Hq + h] != 0 : true;
+        if (sp) {
+          if (cnt == i) myh = h;
+          ++cnt;
+        }
+      }
+      if (cnt == 0) continue;
+      bf16x8 qb[T];
+      {
+        const bf16_bits* qr = a.q + (((size_t)b * a.N + n) * a.Hq + (myh < 0 ? 0 : myh)) * HD;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          uint4 u = (myh >= 0) ? *reinterpret_cast<const uint4*>(qr + q * (HD / 4) + t * 8)
+                               : make_uint4(0, 0, 0, 0);
+          qb[t] = as_bf16x8(u);
+        }
+      }
+      ColState<HD> st;
+      st.m = -INFINITY;
+      st.l = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
+      const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
+      for (int sidx2 = 0; sidx2 < nsteps; ++sidx2) {
+        const int e0 = sidx2 * 32;
+        // value rows of the 32 keys -> this wave's LDS tile
+        constexpr int CPR = HD / 8;
+#pragma unroll
+        for (int x = 0; x < 32 * CPR / 64; ++x) {
+          const int cidx = x * 64 + lane;
+          const int r = cidx / CPR, cc = cidx - r * CPR;
+          const int j = ilist[e0 + r];
+          uint4 vv = make_uint4(0, 0, 0, 0);
+          if (j >= 0) vv = *reinterpret_cast<const uint4*>(vbase + (size_t)j * rstride + cc * 8);
+          *reinterpret_cast<uint4*>(vtile + r * VSTR + cc * 16) = vv;
+        }
+        // key rows straight into the A operand
+        uint4 ka[2][T];
+        bool kval[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = ilist[e0 + u * 16 + i];
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            ka[u][t] = (j >= 0) ? *reinterpret_cast<const uint4*>(kbase + (size_t)j * rstride +
+                                                                   q * (HD / 4) + t * 8)
+                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) kval[u][r] = ilist[e0 + u * 16 + 4 * q + r] >= 0;
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's LDS tile is complete
+        __builtin_amdgcn_wave_barrier();
+        step_core<HD>(ka, qb, kval, vtile, a.scale_log2, st);
+        __builtin_amdgcn_wave_barrier();
+      }
+      const size_t orow = ((size_t)b * a.N + n) * a.Hq + (myh < 0 ? 0 : myh);
+      finish_col<HD>(st, a, orow, myh >= 0);
+    }
+  }
+}
+
+}  // namespace
+
+bool mfma_attention_supported(const Dims& D) {
+  return D.qkv_bf16 && (D.d == 64 || D.d == 128) && D.K <= 2048 && D.Hq / D.Hkv >= 1;
+}
+
+hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& aa, hipStream_t s) {
+  if (D.B == 0 || aa.R == 0) return hipSuccess;
+  MfmaArgs a{};
+  a.q = (const bf16_bits*)aa.q; a.k = (const bf16_bits*)aa.k; a.v = (const bf16_bits*)aa.v;
+  a.topk = aa.topk; a.idx_rows_per_b = aa.idx_rows_per_b; a.idx_n_base = aa.idx_n_base;
+  a.gate = aa.gate; a.y2 = aa.y2; a.route = aa.route; a.out = aa.out;
+  a.B = D.B; a.N = D.N; a.L = D.L; a.Hq = D.Hq; a.Hkv = D.Hkv; a.K = D.K;
+  a.n0 = aa.n0; a.R = aa.R;
+  a.qtiles = (aa.R + 63) / 64;
+  a.scale_log2 = D.scale * kLog2e;
+  const long long dense_max = aa.route ? (long long)D.B * D.Hq * a.qtiles : 0;
+  const long long blocks = dense_max + (long long)D.B * aa.R;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (D.d == 128)
+    hipLaunchKernelGGL(k_attn_mfma<128>, dim3((unsigned)blocks), dim3(MT), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_attn_mfma<64>, dim3((unsigned)blocks), dim3(MT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

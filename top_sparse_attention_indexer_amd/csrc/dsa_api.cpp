@@ -279,6 +279,8 @@ dsa_status dsa_sparse_attn(const dsa_problem* p, const void* q, const void* k, c
   a.n0 = 0; a.R = D.N;
   a.splits_sparse = P.splits_sparse;
   a.splits_dense = P.splits_dense;
+  if (!P.decode && dsa::mfma_attention_supported(D))
+    return hip_status(dsa::launch_attention_mfma(D, a, (hipStream_t)stream), "dsa_sparse_attn");
   return hip_status(dsa::launch_attention(D, a, (hipStream_t)stream), "dsa_sparse_attn");
 }
 
@@ -339,7 +341,10 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
     a.n0 = n0; a.R = R;
     a.splits_sparse = P.splits_sparse;
     a.splits_dense = P.splits_dense;
-    e = dsa::launch_attention(D, a, s);
+    if (!P.decode && dsa::mfma_attention_supported(D))
+      e = dsa::launch_attention_mfma(D, a, s);
+    else
+      e = dsa::launch_attention(D, a, s);
   }
   return hip_status(e, "dsa_fused_forward");
 }

@@ -57,6 +57,10 @@ struct AttnArgs {
 size_t attn_part_bytes(const Dims& D, int R, int splits);
 void attn_pick_splits(const Dims& D, int R, int& splits_sparse, int& splits_dense);
 hipError_t launch_attention(const Dims& D, const AttnArgs& a, hipStream_t s);
+// bf16 MFMA attention for prefill-shaped calls (both routes in one launch;
+// no partials).  Supported for bf16 q/k/v, d in {64, 128}, K <= 2048.
+bool mfma_attention_supported(const Dims& D);
+hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& a, hipStream_t s);
 
 // ---- fused decode (one cooperative launch) ----------------------------------
 struct DecodePlan {
