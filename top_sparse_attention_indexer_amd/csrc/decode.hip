@@ -25,6 +25,9 @@
 //       scores 64 keys (lane = key), online softmax, PV with lane = value
 //       slice; the last split of a (row, KV head, head chunk) merges the
 //       partials and applies the gate.
+#include <unistd.h>
+
+#include <chrono>
 #include <map>
 #include <mutex>
 
@@ -43,16 +46,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct DecodeArgs {
   const void* q_idx; const void* k_idx; const void* q; const void* k; const void* v;
   const float* gate; const float* y2; const uint8_t* route; float* out; int32_t* list;
-  uint32_t* ctl;     // barrier counters, error flag          (zeroed before launch)
-  uint32_t* hist0;   // [rows][2048] first-digit histogram   (zeroed before launch)
-  uint32_t* hist1;   // [rows][2048] second-digit histogram  (zeroed before launch)
-  uint32_t* cand_n;  // [rows] candidate counts              (zeroed before launch)
-  uint32_t* ticket;  // [rows][Hkv][nhc] finished splits     (zeroed before launch)
+  uint64_t* ctl;     // epoch-tagged barrier counters and error word
+  uint64_t* rowtag;  // [rows] epoch-tagged state of the row's zeroed arrays
+  uint32_t* hist0;   // [rows][2048] first-digit histogram   (zeroed in-kernel)
+  uint32_t* hist1;   // [rows][2048] second-digit histogram  (zeroed in-kernel)
+  uint32_t* cand_n;  // [rows] candidate counts              (zeroed in-kernel)
+  uint32_t* ticket;  // [rows][Hkv][nhc] finished splits     (zeroed in-kernel)
   uint32_t* cnt;     // [rows][nch] keys above the first-digit bin, per chunk
   uint64_t* cand;    // [rows][cand_cap]     key << 32 | position
   float* part;       // [rows][Hq][S][HD+2]
   int B, N, L, Hq, Hkv, K, CH, nch, S, nhc, cand_cap;
   float scale_log2;
+  uint32_t epoch;    // distinct per launch; tags every control word
 };
 
 __device__ __forceinline__ bool seq_sparse(const uint8_t* route, int b, int Hq) {
@@ -81,44 +86,97 @@ __device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
 __device__ __forceinline__ void st_devf(float* p, float v) { st_dev((uint32_t*)p, __float_as_uint(v)); }
 __device__ __forceinline__ float ld_devf(const float* p) { return __uint_as_float(ld_dev((const uint32_t*)p)); }
 
-constexpr int kBarGroup = 16;   // workgroups per first-level barrier counter
-// ctl words: [0] second-level counter, [1] error flag, [2] release generation,
-// [64 + 64 * g] first-level counter of group g (one cache line apart).
-size_t ctl_words(int grid) { return 64 + 64 * (size_t)((grid + kBarGroup - 1) / kBarGroup); }
+constexpr int kBarGroup = 16;   // workgroups per first-level barrier group
+// Control block of 64-bit words, each (launch epoch << 32 | value); a word
+// whose epoch is not the current launch's means "nothing yet", so the block
+// is never cleared.  Layout: [0] error word; member slots from word 8 (one
+// per workgroup, grouped 16 to two 64-byte lines); group slots after them,
+// one per 64-byte line.
+size_t ctl_words64(int grid) {
+  const size_t ng = (size_t)(grid + kBarGroup - 1) / kBarGroup;
+  return 8 + ng * kBarGroup + ng * 8;
+}
 
-// Two-level grid barrier with a bounded wait.  Each thread first waits for its
-// own outstanding memory operations, so every store issued before the barrier
-// has completed when the workgroup arrives.  Returns false (and raises the
-// error flag) if the grid did not arrive in time or another workgroup gave up.
-__device__ bool grid_sync(uint32_t* ctl, uint32_t phase, int* flag) {
+__device__ __forceinline__ bool tagged(uint64_t v, uint32_t epoch, uint32_t at_least) {
+  return (uint32_t)(v >> 32) == epoch && (uint32_t)v >= at_least;
+}
+
+__device__ __forceinline__ void raise_error(const DecodeArgs& a) {
+  st_dev64(a.ctl, ((uint64_t)a.epoch << 32) | 1ull);
+}
+
+// Bounded wait of one thread for a tagged word; false on timeout or error.
+__device__ bool wait_tag(const DecodeArgs& a, const uint64_t* p, uint32_t at_least) {
+  uint32_t spins = 0;
+  while (!tagged(ld_dev64(p), a.epoch, at_least)) {
+    if (tagged(ld_dev64(a.ctl), a.epoch, 1u)) return false;
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > (1u << 24)) {
+      raise_error(a);
+      return false;
+    }
+  }
+  return true;
+}
+
+// Two-level grid barrier without shared counters: every workgroup writes its
+// own arrival slot, the first workgroup of each group of 16 waits for its
+// members and writes the group slot, and every workgroup waits for all group
+// slots.  Each thread first waits for its own outstanding memory operations,
+// so the stores before the barrier have completed when the slot is written.
+__device__ bool grid_sync(const DecodeArgs& a, uint32_t phase, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int G = gridDim.x;
-    const int ngroups = (G + kBarGroup - 1) / kBarGroup;
-    const int g = blockIdx.x / kBarGroup;
-    const uint32_t gsize = (uint32_t)min(kBarGroup, G - g * kBarGroup);
-    const uint32_t old = atomicAdd(&ctl[64 + 64 * g], 1u);
-    if (old + 1 == phase * gsize) {
-      const uint32_t o2 = atomicAdd(&ctl[0], 1u);
-      if (o2 + 1 == phase * (uint32_t)ngroups) atomicAdd(&ctl[2], 1u);
-    }
-    int good = 1;
-    uint32_t spins = 0;
-    while (ld_dev(&ctl[2]) < phase) {
-      if (ld_dev(&ctl[1]) != 0u) {
-        good = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > (1u << 24)) {
-        atomicOr(&ctl[1], 1u);
-        good = 0;
-        break;
-      }
-    }
-    *flag = good;
+  const int G = gridDim.x;
+  const int ngroups = (G + kBarGroup - 1) / kBarGroup;
+  const int g = blockIdx.x / kBarGroup;
+  uint64_t* mslot = a.ctl + 8;
+  uint64_t* gslot = a.ctl + 8 + (size_t)ngroups * kBarGroup;
+  const uint64_t tag = ((uint64_t)a.epoch << 32) | phase;
+  if (threadIdx.x == 0) *flag = 1;
+  if (threadIdx.x == 0) st_dev64(mslot + blockIdx.x, tag);
+  __syncthreads();
+  if (blockIdx.x == g * kBarGroup) {
+    const int gsize = min(kBarGroup, G - g * kBarGroup);
+    if ((int)threadIdx.x < gsize && !wait_tag(a, mslot + g * kBarGroup + threadIdx.x, phase))
+      *flag = 0;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0 && *flag) st_dev64(gslot + 8 * g, tag);
   }
+  if ((int)threadIdx.x < ngroups && !wait_tag(a, gslot + 8 * threadIdx.x, phase)) *flag = 0;
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Row accumulators (both histograms, candidate count, merge tickets) are
+// cleared at the start of every launch by the first unit of the sequence;
+// the row's tag then reads "ready" for this launch.
+__device__ void clear_rows(const DecodeArgs& a, int b) {
+  const int nt = a.Hkv * a.nhc;
+  for (int n = 0; n < a.N; ++n) {
+    const int row = b * a.N + n;
+    uint32_t* h0 = a.hist0 + (size_t)row * 2048;
+    uint32_t* h1 = a.hist1 + (size_t)row * 2048;
+    for (int i = threadIdx.x; i < 2048; i += DT) {
+      st_dev(h0 + i, 0u);
+      st_dev(h1 + i, 0u);
+    }
+    for (int i = threadIdx.x; i < nt; i += DT) st_dev(a.ticket + (size_t)row * nt + i, 0u);
+    if (threadIdx.x == 0) st_dev(a.cand_n + row, 0u);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < a.N)
+    st_dev64(a.rowtag + b * a.N + threadIdx.x, ((uint64_t)a.epoch << 32) | 2ull);
+}
+
+// Waits until the rows of sequence b are cleared for this launch.
+__device__ bool rows_ready(const DecodeArgs& a, int b, int* flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = 1;
+  __syncthreads();
+  if ((int)threadIdx.x < a.N && !wait_tag(a, a.rowtag + b * a.N + threadIdx.x, 2u)) *flag = 0;
   __syncthreads();
   return *flag != 0;
 }
@@ -391,6 +449,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
   const bool sp = has_unit && seq_sparse(a.route, b, a.Hq);
   const int N = a.N, K = a.K;
 
+  if (has_unit && c == 0) clear_rows(a, b);
+
   // ---------------------------------------------------------------- P1 scan
   if (sp) {
     constexpr int EPL = 16 / (int)sizeof(TI);
@@ -432,6 +492,10 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
         }
       }
     }
+  }
+  // the sequence's per-row accumulators are cleared by its first unit
+  if (has_unit && !rows_ready(a, b, &flag)) return;
+  if (sp) {
     __syncthreads();
     for (int n = 0; n < N; ++n) {
       const int vis = a.L - N + n + 1;
@@ -448,7 +512,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       __syncthreads();
     }
   }
-  if (!grid_sync(a.ctl, 1u, &flag)) return;
+  if (!grid_sync(a, 1u, &flag)) return;
 
   // ---------------------------------------------------------------- P2 candidates
   // t0 = bin of the K-th key; keys above it are counted per chunk, keys in it
@@ -502,7 +566,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       __syncthreads();
     }
   }
-  if (!grid_sync(a.ctl, 2u, &flag)) return;
+  if (!grid_sync(a, 2u, &flag)) return;
 
   // ---------------------------------------------------------------- P3 select + ordered rows
   // Every unit resolves its row's exact threshold itself (no further
@@ -632,7 +696,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       }
     }
   }
-  if (!grid_sync(a.ctl, 3u, &flag)) return;
+  if (!grid_sync(a, 3u, &flag)) return;
 
   // ---------------------------------------------------------------- P4 attention + merge
   // Items (row, KV head, key split, head chunk).  The last split of a
@@ -829,7 +893,7 @@ size_t decode_ws_bound(const Dims& D) {
 // words, both digit histograms, candidate counts, tickets), then per-chunk
 // counts, candidates and attention partials.
 struct DecodeLayout {
-  size_t ctl, hist0, hist1, cand_n, ticket, zero_end, cnt, cand, part, total;
+  size_t ctl, rowtag, hist0, hist1, cand_n, ticket, cnt, cand, part, total;
 };
 
 DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
@@ -837,12 +901,12 @@ DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   DecodeLayout Lo;
   size_t off = 0;
-  Lo.ctl = off;    off = al(off + ctl_words(kMaxGrid) * 4);
+  Lo.ctl = off;    off = al(off + ctl_words64(kMaxGrid) * 8);
+  Lo.rowtag = off; off = al(off + rows * 8);
   Lo.hist0 = off;  off = al(off + rows * 2048 * 4);
   Lo.hist1 = off;  off = al(off + rows * 2048 * 4);
   Lo.cand_n = off; off = al(off + rows * 4);
   Lo.ticket = off; off = al(off + rows * D.Hkv * (size_t)P.nhc * 4);
-  Lo.zero_end = off;
   Lo.cnt = off;    off = al(off + rows * (size_t)P.nch * 4);
   Lo.cand = off;   off = al(off + rows * (size_t)P.cand_cap * 8);
   Lo.part = off;   off = al(off + rows * D.Hq * (size_t)P.S * (D.d + 2) * 4);
@@ -859,7 +923,19 @@ struct StreamOrder {
   hipStream_t last = nullptr;
   bool have_last = false;
   hipEvent_t done = nullptr;
+  uint32_t epoch = 0;
 };
+
+// A fresh, nonzero launch epoch; the first one is drawn from the clock and
+// the process id so that control words left by another process do not match.
+uint32_t next_epoch(StreamOrder& so) {
+  if (so.epoch == 0) {
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    so.epoch = (uint32_t)(t ^ (t >> 32) ^ ((uint64_t)getpid() << 16));
+  }
+  if (++so.epoch == 0) ++so.epoch;
+  return so.epoch;
+}
 
 StreamOrder& stream_order(int dev) {
   static StreamOrder orders[64];
@@ -875,7 +951,8 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   DecodeArgs a{};
   a.q_idx = q_idx; a.k_idx = k_idx; a.q = q; a.k = k; a.v = v;
   a.gate = gate; a.y2 = y2; a.route = route; a.out = out; a.list = list;
-  a.ctl = (uint32_t*)(w + Lo.ctl);
+  a.ctl = (uint64_t*)(w + Lo.ctl);
+  a.rowtag = (uint64_t*)(w + Lo.rowtag);
   a.hist0 = (uint32_t*)(w + Lo.hist0);
   a.hist1 = (uint32_t*)(w + Lo.hist1);
   a.cand_n = (uint32_t*)(w + Lo.cand_n);
@@ -900,8 +977,7 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
     e = hipStreamWaitEvent(s, so.done, 0);
     if (e != hipSuccess) return e;
   }
-  e = launch_fill_u32((uint32_t*)w, Lo.zero_end / 4, 0u, s);
-  if (e != hipSuccess) return e;
+  a.epoch = next_epoch(so);
   void* args[] = {&a};
   e = hipLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s);
   if (e != hipSuccess) return e;
