@@ -31,6 +31,8 @@
 #include <map>
 #include <mutex>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -39,6 +41,7 @@ namespace {
 
 constexpr int DT = 256;        // threads per workgroup
 constexpr int DSC = 8192;      // LDS score capacity per workgroup (floats)
+constexpr int kLdsFloats = 16384 + 8 * 128 + 64;  // value tiles / scores + q + (max, sum)
 constexpr int DMAXCH = 2048;   // max chunks per sequence
 constexpr int kMaxGrid = 4096;  // largest grid the control block is sized for
 constexpr float kLog2e = 1.4426950408889634f;
@@ -52,8 +55,8 @@ struct DecodeArgs {
   uint32_t* hist1;   // [rows][2048] second-digit histogram  (zeroed in-kernel)
   uint32_t* cand_n;  // [rows] candidate counts              (zeroed in-kernel)
   uint32_t* ticket;  // [rows][Hkv][nhc] finished splits     (zeroed in-kernel)
-  uint32_t* cnt;     // [rows][nch] keys above the first-digit bin, per chunk
-  uint64_t* cand;    // [rows][cand_cap]     key << 32 | position
+  uint32_t* cnt;     // [rows][nch] per chunk: keys above the first-digit bin t0
+  uint64_t* cand;    // [rows][cand_cap] key << 32 | position
   float* part;       // [rows][Hq][S][HD+2]
   int B, N, L, Hq, Hkv, K, CH, nch, S, nhc, cand_cap;
   float scale_log2;
@@ -248,10 +251,14 @@ __device__ __forceinline__ void widen(const uint4& u, float* o, const float*) {
 
 // One attention pass of an item: heads hsel[0..nh) of KV head g, keys given
 // by the index-row segment [e0, e1) (sparse) or positions [e0, e1) (dense).
-// Each wave takes 64 keys at a time: scores with lane = key, online softmax
-// per wave, PV with lane = (key slot, 16-byte slice of the value row).  The
-// four waves are merged through LDS; one partial (max, sum, acc) per head is
-// written for split s.  Loads are issued in batches of 8 per lane.
+// Each wave takes 64 keys at a time: scores with lane = key (all key-row
+// loads in flight together), online softmax per wave, PV with lane = (key
+// slot, 16-byte slice of the value row).  bf16 value rows go straight from
+// memory into this wave's LDS tile (no registers), issued before the scores
+// are computed.  The four waves are merged through LDS; one partial
+// (max, sum, acc) per head is written for split s.
+// LDS use: [0, 16384) floats value tiles (4 x 16 KB, later the merge
+// buffer), then q (HCT x HD) and the per-wave (max, sum).
 template <typename TQ, int HD, int HCT>
 __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
                        int e0, int e1, const int* hsel, int nh, float* lds) {
@@ -259,14 +266,16 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
   constexpr int LPR = HD / EPV;               // lanes per value row
   constexpr int KPI = 64 / LPR;               // value rows per load instruction
   constexpr int NKL = HD / EPV;               // 16-byte loads per key row
+  constexpr bool VLDS = sizeof(TQ) == 2;      // value rows staged in LDS
   constexpr int BATCH = 8;
   const TQ* K = (const TQ*)a.k;
   const TQ* V = (const TQ*)a.v;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int p = a.L - a.N + n;
-  float* qs = lds;                     // [HCT][HD]
-  float* wb = lds + HCT * HD;          // [4][HCT][HD]
-  float* wml = wb + 4 * HCT * HD;      // [4][HCT][2]
+  char* vtile = (char*)lds + w * 64 * HD * 2;  // this wave's 64 value rows (bf16)
+  float* wb = lds;                             // [4][HCT][HD], after the key loop
+  float* qs = lds + 16384;                     // [HCT][HD]
+  float* wml = qs + HCT * HD;                  // [4][HCT][2]
   for (int e = threadIdx.x; e < HCT * HD; e += DT) {
     const int hh = e / HD, c = e - hh * HD;
     float x = 0.f;
@@ -285,6 +294,7 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
   }
   const uint32_t* lrow = (const uint32_t*)a.list + (size_t)row * a.K;
   const int ks = lane / LPR, dc = lane % LPR;
+  const TQ* vseq = V + ((size_t)b * a.L * a.Hkv + g) * HD;
   for (int t0 = e0 + w * 64; t0 < e1; t0 += 4 * 64) {
     const int e = t0 + lane;
     int j = -1;
@@ -292,17 +302,14 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
       j = dense ? e : (int)ld_dev(lrow + e);
       if (j < 0 || j > p) j = -1;
     }
-    // bf16 value rows are fetched before the scores are computed (their
-    // addresses are already known), so their latency overlaps the key work
-    constexpr bool PREF = sizeof(TQ) == 2 && HCT <= 4;
-    constexpr int NVL = 64 / KPI;               // value loads per lane per 64 keys
-    uint4 vraw[PREF ? NVL : 1];
-    if constexpr (PREF) {
+    if constexpr (VLDS) {
+      // rows r = m*KPI + lane/LPR of this wave's tile, 16-byte slice lane%LPR
 #pragma unroll
-      for (int i = 0; i < NVL; ++i) {
-        const int jv = __shfl(j, i * KPI + ks, 64);
-        vraw[i] = (jv >= 0) ? raw16(V + (((size_t)b * a.L + jv) * a.Hkv + g) * HD + dc * EPV)
-                            : make_uint4(0, 0, 0, 0);
+      for (int m = 0; m < 64 / KPI; ++m) {
+        const int jr = __shfl(j, m * KPI + ks, 64);
+        const TQ* src = vseq + (size_t)(jr < 0 ? 0 : jr) * a.Hkv * HD + dc * EPV;
+        __builtin_amdgcn_global_load_lds(
+            (const void*)src, (__attribute__((address_space(3))) void*)(vtile + m * 1024), 16, 0, 0);
       }
     }
     float sc[HCT];
@@ -346,30 +353,35 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
       for (int i = 0; i < EPV; ++i) acc[h][i] *= alpha;
     }
     // PV: lane = (key slot ks, dims dc*EPV ..)
-    if constexpr (PREF) {
-#pragma unroll
-      for (int i = 0; i < NVL; ++i) {
+    if constexpr (VLDS) {
+      __builtin_amdgcn_s_waitcnt(0);      // this wave's value tile has arrived
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+      for (int t = 0; t < 64; t += KPI) {
+        const uint4 u = *reinterpret_cast<const uint4*>(vtile + (t + ks) * (HD * 2) + dc * 16);
         float vv[EPV];
-        widen(vraw[i], vv, (const TQ*)nullptr);
+        widen(u, vv, (const TQ*)nullptr);
 #pragma unroll
         for (int h = 0; h < HCT; ++h) {
-          const float pv = __shfl(pr[h], i * KPI + ks, 64);
+          const float pv = __shfl(pr[h], t + ks, 64);
 #pragma unroll
           for (int x = 0; x < EPV; ++x) acc[h][x] = fmaf(pv, vv[x], acc[h][x]);
         }
       }
+      __builtin_amdgcn_s_waitcnt(0);      // tile reads done before it is refilled
+      __builtin_amdgcn_wave_barrier();
     } else {
 #pragma unroll 1
-      for (int t = 0; t < 64; t += KPI * BATCH) {
-        uint4 raw[BATCH];
+      for (int t = 0; t < 64; t += KPI * 8) {
+        uint4 raw[8];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
+        for (int i = 0; i < 8; ++i) {
           const int jv = __shfl(j, t + i * KPI + ks, 64);
           raw[i] = (jv >= 0) ? raw16(V + (((size_t)b * a.L + jv) * a.Hkv + g) * HD + dc * EPV)
                              : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
+        for (int i = 0; i < 8; ++i) {
           float vv[EPV];
           widen(raw[i], vv, (const TQ*)nullptr);
 #pragma unroll
@@ -389,6 +401,7 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
     for (int h = 0; h < HCT; ++h)
 #pragma unroll
       for (int i = 0; i < EPV; ++i) acc[h][i] += __shfl_xor(acc[h][i], o, 64);
+  __syncthreads();   // value tiles are dead; their LDS becomes the merge buffer
   if (lane < LPR) {
 #pragma unroll
     for (int h = 0; h < HCT; ++h)
@@ -430,7 +443,8 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
 
 template <typename TI, int DIDX, typename TQ, int HD, int HCT>
 __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
-  __shared__ float lds[10240];
+  __shared__ float4 lds4[kLdsFloats / 4];
+  float* lds = reinterpret_cast<float*>(lds4);
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scratch[DT / DSA_WAVE + 1];
   __shared__ uint32_t res[4];
@@ -466,7 +480,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
         qv[n][e] = (n < N) ? ld_f(qi, ((size_t)b * N + n) * DIDX + sub * EPL + e) : 0.f;
-    constexpr int U = 8;
+    constexpr int U = 16;
     for (int base = w * KPW; base < clen; base += 4 * KPW * U) {
       uint4 raw[U];
 #pragma unroll
@@ -542,11 +556,20 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       uint32_t tot_c;
       const uint32_t pre = block_excl_scan<DT>(ncand, scratch, tot_c);
       const uint32_t tot_a = block_sum(above, scratch);
+      uint32_t base_slot = 0;
       if (threadIdx.x == 0) {
-        res[2] = tot_c ? atomicAdd(&a.cand_n[row], tot_c) : 0u;
+        // reserve this unit's candidate slots; the reply is needed only after
+        // the second-digit histogram below
+        if (tot_c) base_slot = atomicAdd(&a.cand_n[row], tot_c);
         st_dev(&a.cnt[(size_t)row * a.nch + c], tot_a);
       }
       for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+      __syncthreads();
+      for (int jj = threadIdx.x; jj < lim; jj += DT) {
+        const uint32_t key = radix_key(lds[n * a.CH + jj]);
+        if ((key >> 21) == t0) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
+      }
+      if (threadIdx.x == 0) res[2] = base_slot;
       __syncthreads();
       uint32_t slot = res[2] + pre;
       uint64_t* cr = (uint64_t*)a.cand + (size_t)row * a.cand_cap;
@@ -556,7 +579,6 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
           if (slot < (uint32_t)a.cand_cap)
             st_dev64(cr + slot, ((uint64_t)key << 32) | (uint32_t)(j0 + jj));
           ++slot;
-          atomicAdd(&hist[(key >> 10) & 2047u], 1u);
         }
       }
       __syncthreads();
@@ -593,44 +615,57 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       }
       const uint32_t t0 = t0s[n];
       uint32_t kk = kk0s[n];
+      // one round trip: second-digit histogram, candidate count, and the keys
+      // above bin t0 in the chunks before this one
       const uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
+      const uint32_t* cnt_row = a.cnt + (size_t)row * a.nch;
+      uint32_t before = 0;
+      {
+        uint32_t h8[2048 / DT];
 #pragma unroll
-      for (int i = 0; i < 2048 / DT; ++i) hist[threadIdx.x + i * DT] = ld_dev(gh1 + threadIdx.x + i * DT);
+        for (int x = 0; x < 2048 / DT; ++x) h8[x] = ld_dev(gh1 + threadIdx.x + x * DT);
+        if (threadIdx.x == 0) res[2] = ld_dev(&a.cand_n[row]);
+        for (int u = threadIdx.x; u < c; u += DT) before += ld_dev(cnt_row + u);
+#pragma unroll
+        for (int x = 0; x < 2048 / DT; ++x) hist[threadIdx.x + x * DT] = h8[x];
+      }
       __syncthreads();
+      const int nc = (int)min(res[2], (uint32_t)a.cand_cap);
       pick_top(hist, 2048, kk, scratch, res);
       const uint32_t t1 = res[0];
       kk -= res[1];
       const uint32_t m = hist[t1];              // candidates sharing digits t0, t1
-      const int nc = (int)min(ld_dev(&a.cand_n[row]), (uint32_t)a.cand_cap);
       const uint64_t* crg = (const uint64_t*)a.cand + (size_t)row * a.cand_cap;
+      auto cand_slot = [&](int f) -> uint32_t { return (uint32_t)f; };
       const uint32_t pfx = (t0 << 11) | t1;      // top 22 bits of T
-      const int cap_lds = (10240 - ((N * a.CH + 1) & ~1)) / 2;
-      uint64_t* cl = (uint64_t*)(lds + ((N * a.CH + 1) & ~1));
+      uint64_t* cl = (uint64_t*)(lds + DSC);
+      const int cap_lds = (kLdsFloats - DSC) / 2;
       const bool in_lds = m <= (uint32_t)cap_lds;
       if (threadIdx.x == 0) res[3] = 0;
       __syncthreads();
       // one pass over the row's candidates: selected-for-sure ones before this
       // chunk, and the ones sharing the top two digits (kept in LDS)
-      uint32_t before = 0;
-      for (int i0 = 0; i0 < nc; i0 += DT * 4) {
-        uint64_t v4[4];
+      for (int i0 = 0; i0 < nc; i0 += DT * 8) {
+        uint64_t v8[8];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int i = i0 + x * DT + threadIdx.x;
-          v4[x] = (i < nc) ? ld_dev64(crg + i) : 0ull;
+        for (int x = 0; x < 8; ++x) {
+          const int f = i0 + x * DT + threadIdx.x;
+          v8[x] = (f < nc) ? ld_dev64(crg + cand_slot(f)) : 0ull;
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int i = i0 + x * DT + threadIdx.x;
-          if (i >= nc) continue;
-          const uint32_t key = (uint32_t)(v4[x] >> 32), pos = (uint32_t)v4[x];
+        for (int x = 0; x < 8; ++x) {
+          const int f = i0 + x * DT + threadIdx.x;
+          if (f >= nc) continue;
+          const uint32_t key = (uint32_t)(v8[x] >> 32), pos = (uint32_t)v8[x];
           const uint32_t top = key >> 10;
           if (top > pfx && pos < (uint32_t)j0) ++before;
-          if (top == pfx && in_lds) cl[atomicAdd(&res[3], 1u)] = v4[x];
+          if (top == pfx && in_lds) cl[atomicAdd(&res[3], 1u)] = v8[x];
         }
       }
       __syncthreads();
-      auto cand = [&](uint32_t i) -> uint64_t { return in_lds ? cl[i] : ld_dev64(crg + i); };
+      auto cand = [&](uint32_t i) -> uint64_t {
+        return in_lds ? cl[i] : ld_dev64(crg + cand_slot((int)i));
+      };
       const uint32_t nl = in_lds ? m : (uint32_t)nc;   // entries to scan for the last digit
       // digit 3: key bits 9..0 among the candidates with prefix pfx
       for (int i = threadIdx.x; i < 1024; i += DT) hist[i] = 0;
@@ -677,9 +712,6 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
         if ((key >> 10) == pfx && pos < (uint32_t)j0 && (key > T || (key == T && pos <= pstar)))
           ++before;
       }
-      // keys in bins above t0 before this chunk
-      const uint32_t* cc = a.cnt + (size_t)row * a.nch;
-      for (int i = threadIdx.x; i < c; i += DT) before += ld_dev(cc + i);
       uint32_t base = block_sum(before, scratch);
       const int lim = min(clen, vis - j0);
       for (int s0 = 0; s0 < lim; s0 += DT) {
@@ -979,9 +1011,8 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   }
   a.epoch = next_epoch(so);
   void* args[] = {&a};
-  e = hipLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s);
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(so.done, s);
+  // the completion event rides on the kernel's own dispatch
+  e = hipExtLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s, nullptr, so.done, 0);
   so.last = s;
   so.have_last = true;
   return e;
