@@ -61,6 +61,28 @@ def algorithmic_work(w, route):
     return byt, flops
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the counter runs kept in
+    profiles/traffic.json (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, each
+    scaled by the factor a plain copy of known size gives).  None when no
+    record exists or the kernel's source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None, None
+    rec = json.load(open(path)).get(workload)
+    if not rec:
+        return None, None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src):
+        return None, rec
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec["source_sha256"]:
+        return None, rec
+    byt = rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]
+    return byt, rec
+
+
 def cpu_baseline(w, x, budget_s):
     """The oracle as it stands, on whole query rows of the same workload, for ~budget_s."""
     from oracle import dsa_oracle as O
@@ -150,6 +172,11 @@ def main():
     tokens = w.batch * w.n_q
     byt, flops = algorithmic_work(w, x["route"])
     achieved = byt / (ms / 1e3) / 1e9
+    traffic, rec = measured_traffic(w.name)
+    if w.n_q <= 4:
+        kernel = "k_decode (the step is this one launch)"
+    else:
+        kernel = "whole step (indexer, top-k and attention launches per chunk of rows)"
     res = {
         "metric": METRIC, "value": tokens / (ms / 1e3), "unit": "query tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -159,9 +186,9 @@ def main():
                    "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim, "idx_dim": w.idx_dim,
                    "top_k": w.top_k, "parallelism": "single GPU"},
         "step_ms_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
-        "roofline": {"bound": "hbm", "kernel": "whole fused step", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": byt, "algorithmic_flops": flops},
+                     "traffic": traffic, "algorithmic_bytes": byt, "algorithmic_flops": flops},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
