@@ -99,7 +99,7 @@ def test_null_and_misaligned_pointers_are_rejected_before_launch():
     a[6] = None           # gate given, y2 missing
     assert lib.dsa_fused_forward(p, *a, None, FAKE, ws_n, None) == B.DSA_ERR_INVALID_ARG
     assert lib.dsa_fused_forward(p, *full, MISALIGNED, FAKE, ws_n, None) == B.DSA_ERR_INVALID_ARG
-    assert lib.dsa_fused_forward(p, *full, None, FAKE, ws_n - 1, None) == B.DSA_ERR_WORKSPACE
+    assert lib.dsa_fused_forward(p, *full, None, FAKE, 16, None) == B.DSA_ERR_WORKSPACE
     assert lib.dsa_fused_forward(p, *full, None, None, ws_n, None) == B.DSA_ERR_WORKSPACE
     assert lib.dsa_fused_forward(p, *full, None, MISALIGNED, ws_n, None) == B.DSA_ERR_INVALID_ARG
 

@@ -45,6 +45,7 @@ constexpr int kLdsFloats = 16384 + 8 * 128 + 64;  // value tiles / scores + q + 
 constexpr int DMAXCH = 2048;   // max chunks per sequence
 constexpr int kMaxGrid = 4096;  // largest grid the control block is sized for
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kCoherentLoad = 16;   // cache policy of a device-coherent load (sc1)
 
 struct DecodeArgs {
   const void* q_idx; const void* k_idx; const void* q; const void* k; const void* v;
@@ -53,11 +54,11 @@ struct DecodeArgs {
   uint64_t* rowtag;  // [rows] epoch-tagged state of the row's zeroed arrays
   uint32_t* hist0;   // [rows][2048] first-digit histogram   (zeroed in-kernel)
   uint32_t* hist1;   // [rows][2048] second-digit histogram  (zeroed in-kernel)
-  uint32_t* cand_n;  // [rows] candidate counts              (zeroed in-kernel)
   uint32_t* ticket;  // [rows][Hkv][nhc] finished splits     (zeroed in-kernel)
+  uint32_t* cand_n;  // [rows][kCandGroups] candidates per group   (zeroed in-kernel)
   uint32_t* cnt;     // [rows][nch] per chunk: keys above the first-digit bin t0
-  uint64_t* cand;    // [rows][cand_cap] key << 32 | position
-  float* part;       // [rows][Hq][S][HD+2]
+  uint64_t* cand;    // [rows][cand_cap] key << 32 | position, one region per group
+  float* part;       // [rows][Hq][S][HD+4]: max, sum, 2 pad, accumulator
   int B, N, L, Hq, Hkv, K, CH, nch, S, nhc, cand_cap;
   float scale_log2;
   uint32_t epoch;    // distinct per launch; tags every control word
@@ -90,6 +91,10 @@ __device__ __forceinline__ void st_devf(float* p, float v) { st_dev((uint32_t*)p
 __device__ __forceinline__ float ld_devf(const float* p) { return __uint_as_float(ld_dev((const uint32_t*)p)); }
 
 constexpr int kBarGroup = 16;   // workgroups per first-level barrier group
+// Candidates of a row are appended to kCandGroups regions, one per group of
+// consecutive chunks, each with its own counter: few chunks contend for a
+// counter and the regions stay contiguous for the readers.
+constexpr int kCandGroups = 16;
 // Control block of 64-bit words, each (launch epoch << 32 | value); a word
 // whose epoch is not the current launch's means "nothing yet", so the block
 // is never cleared.  Layout: [0] error word; member slots from word 8 (one
@@ -166,7 +171,7 @@ __device__ void clear_rows(const DecodeArgs& a, int b) {
       st_dev(h1 + i, 0u);
     }
     for (int i = threadIdx.x; i < nt; i += DT) st_dev(a.ticket + (size_t)row * nt + i, 0u);
-    if (threadIdx.x == 0) st_dev(a.cand_n + row, 0u);
+    if (threadIdx.x < kCandGroups) st_dev(a.cand_n + (size_t)row * kCandGroups + threadIdx.x, 0u);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -261,7 +266,7 @@ __device__ __forceinline__ void widen(const uint4& u, float* o, const float*) {
 // buffer), then q (HCT x HD) and the per-wave (max, sum).
 template <typename TQ, int HD, int HCT>
 __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
-                       int e0, int e1, const int* hsel, int nh, float* lds) {
+                       int e0, int e1, const int* hsel, int nh, float* lds, bool q_ready) {
   constexpr int EPV = 16 / (int)sizeof(TQ);   // elements per 16-byte load
   constexpr int LPR = HD / EPV;               // lanes per value row
   constexpr int KPI = 64 / LPR;               // value rows per load instruction
@@ -276,14 +281,16 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
   float* wb = lds;                             // [4][HCT][HD], after the key loop
   float* qs = lds + 16384;                     // [HCT][HD]
   float* wml = qs + HCT * HD;                  // [4][HCT][2]
-  for (int e = threadIdx.x; e < HCT * HD; e += DT) {
-    const int hh = e / HD, c = e - hh * HD;
-    float x = 0.f;
-    if (hh < nh) x = ld_f((const TQ*)a.q, (((size_t)b * a.N + n) * a.Hq + hsel[hh]) * HD + c) *
-                     a.scale_log2;
-    qs[e] = x;
+  if (!q_ready) {
+    for (int e = threadIdx.x; e < HCT * HD; e += DT) {
+      const int hh = e / HD, c = e - hh * HD;
+      float x = 0.f;
+      if (hh < nh) x = ld_f((const TQ*)a.q, (((size_t)b * a.N + n) * a.Hq + hsel[hh]) * HD + c) *
+                       a.scale_log2;
+      qs[e] = x;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   float m_w[HCT], l_w[HCT], acc[HCT][EPV];
 #pragma unroll
   for (int h = 0; h < HCT; ++h) {
@@ -431,8 +438,8 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
         s_acc = fmaf(f, wb[(ww * HCT + hh) * HD + c], s_acc);
       }
     }
-    float* pp = a.part + (((size_t)row * a.Hq + hsel[hh]) * a.S + s) * (HD + 2);
-    st_devf(pp + 2 + c, s_acc);
+    float* pp = a.part + (((size_t)row * a.Hq + hsel[hh]) * a.S + s) * (HD + 4);
+    st_devf(pp + 4 + c, s_acc);
     if (c == 0) {
       st_devf(pp + 0, M);
       st_devf(pp + 1, l);
@@ -441,8 +448,42 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
   __syncthreads();
 }
 
+// Attention item `it`: (row, KV head g, key split s, head chunk hci), the
+// split index varying fastest so that the splits of one (row, KV head, head
+// chunk) run side by side.
+struct Item {
+  int row, g, s, hci;
+};
+__device__ __forceinline__ Item item_of(const DecodeArgs& a, int it) {
+  Item t;
+  int rem = it;
+  t.s = rem % a.S; rem /= a.S;
+  t.hci = rem % a.nhc; rem /= a.nhc;
+  t.g = rem % a.Hkv; rem /= a.Hkv;
+  t.row = rem;
+  return t;
+}
+
+// The item's query heads by route: sparse ones in hsel[0], dense ones in
+// hsel[1] (thread 0 writes them; the caller synchronises).
+template <int HCT>
+__device__ void item_heads(const DecodeArgs& a, const Item& t, int rb, int (*hsel)[HCT],
+                           int* nsel) {
+  if (threadIdx.x != 0) return;
+  const int G_heads = a.Hq / a.Hkv;
+  int ns = 0, nd = 0;
+  for (int i = t.hci * HCT; i < min(G_heads, t.hci * HCT + HCT); ++i) {
+    const int h = t.g * G_heads + i;
+    const bool sparse = a.route ? (a.route[(size_t)rb * a.Hq + h] != 0) : true;
+    if (sparse) hsel[0][ns++] = h;
+    else hsel[1][nd++] = h;
+  }
+  nsel[0] = ns;
+  nsel[1] = nd;
+}
+
 template <typename TI, int DIDX, typename TQ, int HD, int HCT>
-__global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
+__global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
   __shared__ float4 lds4[kLdsFloats / 4];
   float* lds = reinterpret_cast<float*>(lds4);
   __shared__ uint32_t hist[2048];
@@ -556,11 +597,13 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       uint32_t tot_c;
       const uint32_t pre = block_excl_scan<DT>(ncand, scratch, tot_c);
       const uint32_t tot_a = block_sum(above, scratch);
+      const int upg = (a.nch + kCandGroups - 1) / kCandGroups;   // chunks per group
+      const int grp = c / upg;
       uint32_t base_slot = 0;
       if (threadIdx.x == 0) {
-        // reserve this unit's candidate slots; the reply is needed only after
-        // the second-digit histogram below
-        if (tot_c) base_slot = atomicAdd(&a.cand_n[row], tot_c);
+        // reserve this unit's slots in its group's region; the reply is
+        // needed only after the second-digit histogram below
+        if (tot_c) base_slot = atomicAdd(&a.cand_n[(size_t)row * kCandGroups + grp], tot_c);
         st_dev(&a.cnt[(size_t)row * a.nch + c], tot_a);
       }
       for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
@@ -572,12 +615,11 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       if (threadIdx.x == 0) res[2] = base_slot;
       __syncthreads();
       uint32_t slot = res[2] + pre;
-      uint64_t* cr = (uint64_t*)a.cand + (size_t)row * a.cand_cap;
+      uint64_t* cr = (uint64_t*)a.cand + (size_t)row * a.cand_cap + (size_t)grp * upg * a.CH;
       for (int jj = threadIdx.x; jj < lim; jj += DT) {
         const uint32_t key = radix_key(lds[n * a.CH + jj]);
         if ((key >> 21) == t0) {
-          if (slot < (uint32_t)a.cand_cap)
-            st_dev64(cr + slot, ((uint64_t)key << 32) | (uint32_t)(j0 + jj));
+          st_dev64(cr + slot, ((uint64_t)key << 32) | (uint32_t)(j0 + jj));
           ++slot;
         }
       }
@@ -589,6 +631,30 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
     }
   }
   if (!grid_sync(a, 2u, &flag)) return;
+
+  // q of this workgroup's first attention item: loaded now, moved to LDS once
+  // the selection below no longer needs that LDS
+  constexpr int NQ = (HCT * HD + DT - 1) / DT;
+  const int items = a.B * N * a.Hkv * a.S * a.nhc;
+  const bool q_pre = (int)blockIdx.x < items;
+  float qreg[NQ];
+  if (q_pre) {
+    const Item t = item_of(a, blockIdx.x);
+    const int rb = t.row / N, rn = t.row - rb * N;
+    item_heads<HCT>(a, t, rb, hsel, nsel);
+    __syncthreads();
+    const int set = nsel[0] > 0 ? 0 : 1;
+    const int nh = nsel[set];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int e = threadIdx.x + k * DT;
+      const int hh = e / HD, cq = e - hh * HD;
+      qreg[k] = (e < HCT * HD && hh < nh)
+                    ? ld_f((const TQ*)a.q, (((size_t)rb * N + rn) * a.Hq + hsel[set][hh]) * HD + cq) *
+                          a.scale_log2
+                    : 0.f;
+    }
+  }
 
   // ---------------------------------------------------------------- P3 select + ordered rows
   // Every unit resolves its row's exact threshold itself (no further
@@ -615,42 +681,70 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       }
       const uint32_t t0 = t0s[n];
       uint32_t kk = kk0s[n];
-      // one round trip: second-digit histogram, candidate count, and the keys
-      // above bin t0 in the chunks before this one
+      // one round trip: second-digit histogram, the groups' candidate counts
+      // and the keys above bin t0 in the chunks before this one
       const uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
       const uint32_t* cnt_row = a.cnt + (size_t)row * a.nch;
+      uint32_t* gpre = reinterpret_cast<uint32_t*>(lds + DSC);   // [kCandGroups + 1]
+      uint64_t* cl = reinterpret_cast<uint64_t*>(lds + DSC + 64);
+      const int cap_lds = (kLdsFloats - DSC - 64) / 2;
+      const int upg = (a.nch + kCandGroups - 1) / kCandGroups;
       uint32_t before = 0;
       {
         uint32_t h8[2048 / DT];
 #pragma unroll
         for (int x = 0; x < 2048 / DT; ++x) h8[x] = ld_dev(gh1 + threadIdx.x + x * DT);
-        if (threadIdx.x == 0) res[2] = ld_dev(&a.cand_n[row]);
+        uint32_t gc = 0;
+        if (threadIdx.x < kCandGroups) gc = ld_dev(a.cand_n + (size_t)row * kCandGroups + threadIdx.x);
         for (int u = threadIdx.x; u < c; u += DT) before += ld_dev(cnt_row + u);
 #pragma unroll
         for (int x = 0; x < 2048 / DT; ++x) hist[threadIdx.x + x * DT] = h8[x];
+        if (threadIdx.x < kCandGroups) gpre[threadIdx.x + 1] = gc;
       }
       __syncthreads();
-      const int nc = (int)min(res[2], (uint32_t)a.cand_cap);
+      if (threadIdx.x == 0) {
+        uint32_t acc = 0;
+        gpre[0] = 0;
+        for (int g2 = 1; g2 <= kCandGroups; ++g2) {
+          acc += gpre[g2];
+          gpre[g2] = acc;
+        }
+      }
+      __syncthreads();
+      const int nc = (int)gpre[kCandGroups];
       pick_top(hist, 2048, kk, scratch, res);
       const uint32_t t1 = res[0];
       kk -= res[1];
       const uint32_t m = hist[t1];              // candidates sharing digits t0, t1
       const uint64_t* crg = (const uint64_t*)a.cand + (size_t)row * a.cand_cap;
-      auto cand_slot = [&](int f) -> uint32_t { return (uint32_t)f; };
+      // flat candidate index -> slot: the last group whose first index is <= f
+      // (a fixed-step search, so that several of them interleave)
+      auto grp_of = [&](uint32_t f) -> int {
+        int lo = 0;
+#pragma unroll
+        for (int st = kCandGroups / 2; st > 0; st >>= 1)
+          if (gpre[lo + st] <= f) lo += st;
+        return lo;
+      };
+      auto cand_slot = [&](uint32_t f) -> size_t {
+        const int g2 = grp_of(f);
+        return (size_t)g2 * upg * a.CH + (f - gpre[g2]);
+      };
       const uint32_t pfx = (t0 << 11) | t1;      // top 22 bits of T
-      uint64_t* cl = (uint64_t*)(lds + DSC);
-      const int cap_lds = (kLdsFloats - DSC) / 2;
       const bool in_lds = m <= (uint32_t)cap_lds;
       if (threadIdx.x == 0) res[3] = 0;
       __syncthreads();
       // one pass over the row's candidates: selected-for-sure ones before this
       // chunk, and the ones sharing the top two digits (kept in LDS)
       for (int i0 = 0; i0 < nc; i0 += DT * 8) {
+        size_t sl8[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) sl8[x] = cand_slot((uint32_t)(i0 + x * DT + threadIdx.x));
         uint64_t v8[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int f = i0 + x * DT + threadIdx.x;
-          v8[x] = (f < nc) ? ld_dev64(crg + cand_slot(f)) : 0ull;
+          v8[x] = (f < nc) ? ld_dev64(crg + sl8[x]) : 0ull;
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
@@ -664,46 +758,72 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       }
       __syncthreads();
       auto cand = [&](uint32_t i) -> uint64_t {
-        return in_lds ? cl[i] : ld_dev64(crg + cand_slot((int)i));
+        return in_lds ? cl[i] : ld_dev64(crg + cand_slot(i));
       };
       const uint32_t nl = in_lds ? m : (uint32_t)nc;   // entries to scan for the last digit
-      // digit 3: key bits 9..0 among the candidates with prefix pfx
-      for (int i = threadIdx.x; i < 1024; i += DT) hist[i] = 0;
-      __syncthreads();
-      for (uint32_t i = threadIdx.x; i < nl; i += DT) {
-        const uint32_t key = (uint32_t)(cand(i) >> 32);
-        if ((key >> 10) == pfx) atomicAdd(&hist[key & 1023u], 1u);
-      }
-      __syncthreads();
-      pick_top(hist, 1024, kk, scratch, res);
-      const uint32_t t2 = res[0];
-      kk -= res[1];
-      const uint32_t ties = hist[t2];
-      const uint32_t T = (pfx << 10) | t2;
-      __syncthreads();
-      uint32_t pstar = 0x7fffffffu;
-      if (kk < ties) {
-        // kk-th smallest position among the keys equal to T
-        uint32_t pprefix = 0, pmask = 0;
-        const int pshift[3] = {20, 10, 0};
-        const int pbins[3] = {2048, 1024, 1024};
-        for (int lv = 0; lv < 3; ++lv) {
-          const int nb = pbins[lv], sh = pshift[lv];
-          for (int i = threadIdx.x; i < nb; i += DT) hist[i] = 0;
-          __syncthreads();
-          for (uint32_t i = threadIdx.x; i < nl; i += DT) {
-            const uint64_t cd = cand(i);
-            const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
-            if (key == T && (pos & pmask) == pprefix) atomicAdd(&hist[(pos >> sh) & (nb - 1)], 1u);
+      // T, the K-th key, and P*, the last position taken among keys equal to T
+      uint32_t T, pstar;
+      if (in_lds && m <= (uint32_t)DT) {
+        // few candidates share the top 22 bits: the kk-th of them under
+        // (key descending, position ascending) by counting the ones before it
+        if (threadIdx.x < m) {
+          const uint64_t me = cl[threadIdx.x];
+          const uint32_t key = (uint32_t)(me >> 32), pos = (uint32_t)me;
+          uint32_t r = 0;
+#pragma unroll 8
+          for (uint32_t i = 0; i < m; ++i) {
+            const uint64_t o = cl[i];
+            const uint32_t ok = (uint32_t)(o >> 32), op = (uint32_t)o;
+            r += (ok > key) || (ok == key && op < pos);
           }
-          __syncthreads();
-          pick_low(hist, nb, kk, scratch, res);
-          pprefix |= res[0] << sh;
-          pmask |= (uint32_t)(nb - 1) << sh;
-          kk -= res[1];
-          __syncthreads();
+          if (r + 1 == kk) {
+            res[0] = key;
+            res[1] = pos;
+          }
         }
-        pstar = pprefix;
+        __syncthreads();
+        T = res[0];
+        pstar = res[1];
+        __syncthreads();
+      } else {
+        // digit 3: key bits 9..0 among the candidates with prefix pfx
+        for (int i = threadIdx.x; i < 1024; i += DT) hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+          const uint32_t key = (uint32_t)(cand(i) >> 32);
+          if ((key >> 10) == pfx) atomicAdd(&hist[key & 1023u], 1u);
+        }
+        __syncthreads();
+        pick_top(hist, 1024, kk, scratch, res);
+        const uint32_t t2 = res[0];
+        kk -= res[1];
+        const uint32_t ties = hist[t2];
+        T = (pfx << 10) | t2;
+        __syncthreads();
+        pstar = 0x7fffffffu;
+        if (kk < ties) {
+          // kk-th smallest position among the keys equal to T
+          uint32_t pprefix = 0, pmask = 0;
+          const int pshift[3] = {20, 10, 0};
+          const int pbins[3] = {2048, 1024, 1024};
+          for (int lv = 0; lv < 3; ++lv) {
+            const int nb = pbins[lv], sh = pshift[lv];
+            for (int i = threadIdx.x; i < nb; i += DT) hist[i] = 0;
+            __syncthreads();
+            for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+              const uint64_t cd = cand(i);
+              const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
+              if (key == T && (pos & pmask) == pprefix) atomicAdd(&hist[(pos >> sh) & (nb - 1)], 1u);
+            }
+            __syncthreads();
+            pick_low(hist, nb, kk, scratch, res);
+            pprefix |= res[0] << sh;
+            pmask |= (uint32_t)(nb - 1) << sh;
+            kk -= res[1];
+            __syncthreads();
+          }
+          pstar = pprefix;
+        }
       }
       // selected candidates with the top-two-digit prefix before this chunk
       for (uint32_t i = threadIdx.x; i < nl; i += DT) {
@@ -714,119 +834,154 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeArgs a) {
       }
       uint32_t base = block_sum(before, scratch);
       const int lim = min(clen, vis - j0);
-      for (int s0 = 0; s0 < lim; s0 += DT) {
-        const int jj = s0 + threadIdx.x;
-        bool sel = false;
-        if (jj < lim) {
-          const uint32_t key = radix_key(lds[n * a.CH + jj]);
-          sel = key > T || (key == T && (uint32_t)(j0 + jj) <= pstar);
+      // each thread takes 8 consecutive keys: one block scan per 8 * DT keys
+      for (int s0 = 0; s0 < lim; s0 += DT * 8) {
+        const int jb = s0 + threadIdx.x * 8;
+        uint32_t m8 = 0, c8 = 0;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int jj = jb + x;
+          if (jj < lim) {
+            const uint32_t key = radix_key(lds[n * a.CH + jj]);
+            if (key > T || (key == T && (uint32_t)(j0 + jj) <= pstar)) {
+              m8 |= 1u << x;
+              ++c8;
+            }
+          }
         }
         uint32_t tot;
-        const uint32_t rk = block_rank<DT>(sel, scratch, tot);
-        if (sel && base + rk < (uint32_t)K) st_dev(lr + base + rk, (uint32_t)(j0 + jj));
+        uint32_t o = base + block_excl_scan<DT>(c8, scratch, tot);
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          if ((m8 >> x) & 1u) {
+            if (o < (uint32_t)K) st_dev(lr + o, (uint32_t)(j0 + jb + x));
+            ++o;
+          }
         base += tot;
       }
+    }
+  }
+  if (q_pre) {
+    __syncthreads();
+    float* qs = lds + 16384;
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int e = threadIdx.x + k * DT;
+      if (e < HCT * HD) qs[e] = qreg[k];
     }
   }
   if (!grid_sync(a, 3u, &flag)) return;
 
   // ---------------------------------------------------------------- P4 attention + merge
-  // Items (row, KV head, key split, head chunk).  The last split of a
-  // (row, KV head, head chunk) to finish merges the partials and applies the
-  // gate (ticket counter), so no further grid barrier is needed.
+  // The last split of a (row, KV head, head chunk) to finish merges the
+  // partials and applies the gate (ticket counter), so no further grid
+  // barrier is needed.
   {
-    const int G_heads = a.Hq / a.Hkv;
-    const int items = a.B * N * a.Hkv * a.S * a.nhc;
     const int per_s = ((K + a.S - 1) / a.S + 63) / 64 * 64;
     const int per_d = ((a.L + a.S - 1) / a.S + 63) / 64 * 64;
     for (int it = blockIdx.x; it < items; it += G) {
-      // split index is the fastest-varying so that the splits of one
-      // (row, KV head, head chunk) run side by side
-      int rem = it;
-      const int s = rem % a.S; rem /= a.S;
-      const int hci = rem % a.nhc; rem /= a.nhc;
-      const int g = rem % a.Hkv; rem /= a.Hkv;
-      const int row = rem;
+      const Item t = item_of(a, it);
+      const int row = t.row, g = t.g, s = t.s, hci = t.hci;
       const int rb = row / N, rn = row - rb * N;
-      if (threadIdx.x == 0) {
-        int ns = 0, nd = 0;
-        for (int i = hci * HCT; i < min(G_heads, hci * HCT + HCT); ++i) {
-          const int h = g * G_heads + i;
-          const bool sparse = a.route ? (a.route[(size_t)rb * a.Hq + h] != 0) : true;
-          if (sparse) hsel[0][ns++] = h;
-          else hsel[1][nd++] = h;
-        }
-        nsel[0] = ns;
-        nsel[1] = nd;
-      }
+      item_heads<HCT>(a, t, rb, hsel, nsel);
       __syncthreads();
       const int ns = nsel[0], nd = nsel[1];
       const int vis = a.L - N + rn + 1;
+      const bool first = it == (int)blockIdx.x;   // q already in LDS
       if (ns > 0) {
         const int e0 = s * per_s, e1 = min(K, e0 + per_s);
-        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds);
+        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds, first);
       }
       if (nd > 0) {
         const int e0 = s * per_d, e1 = min(vis, e0 + per_d);
-        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds);
+        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds,
+                            first && ns == 0);
       }
       // ticket: the last split of this (row, g, hci) merges
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
-        const uint32_t t = atomicAdd(&a.ticket[((size_t)row * a.Hkv + g) * a.nhc + hci], 1u);
-        res[0] = (t + 1 == (uint32_t)a.S) ? 1u : 0u;
+        const uint32_t tk = atomicAdd(&a.ticket[((size_t)row * a.Hkv + g) * a.nhc + hci], 1u);
+        res[0] = (tk + 1 == (uint32_t)a.S) ? 1u : 0u;
       }
       __syncthreads();
       if (res[0]) {
-        // stage every split's (max, sum) in LDS, then the weighted sum of the
-        // accumulators with the loads of 8 splits in flight per thread
+        // The partials of the item's heads go straight from memory into LDS
+        // (16-byte pieces, coherent loads, no registers), together with this
+        // thread's gate and second-branch values; then each thread merges its
+        // (head, dim) elements over the splits with a running max.
+        constexpr int PS = HD + 4;                   // floats per partial
+        constexpr int CPP = PS / 4;                  // 16-byte pieces per partial
+        constexpr int NE = (HCT * HD + DT - 1) / DT;
         const int nh = ns + nd;
         const int S = a.S;
-        float* mls = lds;                  // [nh][S][2]
-        float* wts = mls + nh * S * 2;     // [nh][S]
-        float* lsum = wts + nh * S;        // [nh]
-        for (int e = threadIdx.x; e < nh * S; e += DT) {
-          const int hh = e / S, s2 = e - hh * S;
-          const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
-          const float* pp = a.part + (((size_t)row * a.Hq + h) * S + s2) * (HD + 2);
-          mls[2 * e] = ld_devf(pp);
-          mls[2 * e + 1] = ld_devf(pp + 1);
+        const int SB = max(1, min(S, 16384 / (nh * PS)));   // splits per LDS batch
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        float Mx[NE], Lx[NE], Ax[NE], gv[NE], yv[NE];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+          const int e = threadIdx.x + k * DT;
+          const int hh = e / HD, cth = e - hh * HD;
+          const bool ok = e < nh * HD;
+          const int h = !ok ? 0 : (hh < ns ? hsel[0][hh] : hsel[1][hh - ns]);
+          const size_t orow = (size_t)row * a.Hq + h;
+          const bool gk = ok && a.gate;
+          gv[k] = gk ? a.gate[orow] : 1.f;
+          yv[k] = gk ? a.y2[orow * HD + cth] : 0.f;
+          Mx[k] = -INFINITY;
+          Lx[k] = 0.f;
+          Ax[k] = 0.f;
         }
-        __syncthreads();
-        for (int hh = threadIdx.x; hh < nh; hh += DT) {
-          float M = -INFINITY;
-          for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, mls[2 * (hh * S + s2)]);
-          float l = 0.f;
-          for (int s2 = 0; s2 < S; ++s2) {
-            const float ms = mls[2 * (hh * S + s2)];
-            const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-            wts[hh * S + s2] = f;
-            l = fmaf(f, mls[2 * (hh * S + s2) + 1], l);
+        for (int s0 = 0; s0 < S; s0 += SB) {
+          const int sb = min(SB, S - s0);
+          const int npieces = nh * sb * CPP;
+          for (int c0 = w * 64; c0 < npieces; c0 += DT) {
+            const int ci = c0 + lane;
+            if (ci < npieces) {
+              const int hh = ci / (sb * CPP);
+              const int rem = ci - hh * sb * CPP;
+              const int sl = rem / CPP, cc = rem - sl * CPP;
+              const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
+              const float* src = a.part + (((size_t)row * a.Hq + h) * S + s0 + sl) * PS + cc * 4;
+              __builtin_amdgcn_global_load_lds(
+                  (const void*)src, (__attribute__((address_space(3))) void*)(lds + c0 * 4), 16, 0,
+                  kCoherentLoad);
+            }
           }
-          lsum[hh] = l;
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+#pragma unroll
+          for (int k = 0; k < NE; ++k) {
+            const int e = threadIdx.x + k * DT;
+            if (e >= nh * HD) continue;
+            const int hh = e / HD, cth = e - hh * HD;
+            const float* pl = lds + hh * sb * PS;
+            float mb = Mx[k];
+            for (int sl = 0; sl < sb; ++sl) mb = fmaxf(mb, pl[sl * PS]);
+            if (mb == -INFINITY) continue;
+            const float f0 = (Mx[k] == -INFINITY) ? 0.f : exp2f(Mx[k] - mb);
+            float l = Lx[k] * f0, acc = Ax[k] * f0;
+            for (int sl = 0; sl < sb; ++sl) {
+              const float ms = pl[sl * PS];
+              const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mb);
+              l = fmaf(f, pl[sl * PS + 1], l);
+              acc = fmaf(f, pl[sl * PS + 4 + cth], acc);
+            }
+            Mx[k] = mb;
+            Lx[k] = l;
+            Ax[k] = acc;
+          }
+          __syncthreads();
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < nh * HD; e += DT) {
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+          const int e = threadIdx.x + k * DT;
+          if (e >= nh * HD) continue;
           const int hh = e / HD, cth = e - hh * HD;
           const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
-          const float* pp = a.part + ((size_t)row * a.Hq + h) * S * (HD + 2) + 2 + cth;
-          float acc = 0.f;
-          for (int s0 = 0; s0 < S; s0 += 8) {
-            float v8[8];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) v8[x] = (s0 + x < S) ? ld_devf(pp + (s0 + x) * (HD + 2)) : 0.f;
-#pragma unroll
-            for (int x = 0; x < 8; ++x)
-              if (s0 + x < S) acc = fmaf(wts[hh * S + s0 + x], v8[x], acc);
-          }
-          const float l = lsum[hh];
-          float val = (l > 0.f) ? acc / l : 0.f;
           const size_t orow = (size_t)row * a.Hq + h;
-          if (a.gate) {
-            const float gg = a.gate[orow];
-            val = fmaf(gg, val, (1.f - gg) * a.y2[orow * HD + cth]);
-          }
+          float val = (Lx[k] > 0.f) ? Ax[k] / Lx[k] : 0.f;
+          if (a.gate) val = fmaf(gv[k], val, (1.f - gv[k]) * yv[k]);
           a.out[orow * HD + cth] = val;
         }
       }
@@ -902,12 +1057,10 @@ bool decode_plan(const Dims& D, int grid, DecodePlan& P) {
   const int G = D.Hq / D.Hkv;
   const int hct = G <= 4 ? 4 : 8;
   P.nhc = (G + hct - 1) / hct;
-  const long long base_items = (long long)rows * D.Hkv * P.nhc;
-  long long S = (D.K + 255) / 256;
-  const long long smax = (D.K + 63) / 64;
-  while (S < smax && base_items * S * 2 <= grid) S *= 2;
-  P.S = (int)std::min(S, smax);
-  P.cand_cap = D.L;
+  // one split per 256 keys: every split keeps the four waves of its
+  // workgroup busy with one 64-key pass each
+  P.S = std::max(1, (D.K + 255) / 256);
+  P.cand_cap = kCandGroups * ((nch + kCandGroups - 1) / kCandGroups) * (int)ch;
   return true;
 }
 
@@ -917,7 +1070,8 @@ size_t decode_ws_bound(const Dims& D) {
   DecodePlan P;
   P.nch = (int)std::min<long long>(DMAXCH, ((long long)D.L + 255) / 256);
   P.S = (D.K + 63) / 64;
-  P.cand_cap = D.L;
+  P.nhc = D.Hq;
+  P.cand_cap = D.L + kCandGroups * DSC;   // groups * (chunks per group) * CH < L + groups * CH
   return decode_ws_bytes(D, P);
 }
 
@@ -937,11 +1091,11 @@ DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
   Lo.rowtag = off; off = al(off + rows * 8);
   Lo.hist0 = off;  off = al(off + rows * 2048 * 4);
   Lo.hist1 = off;  off = al(off + rows * 2048 * 4);
-  Lo.cand_n = off; off = al(off + rows * 4);
+  Lo.cand_n = off; off = al(off + rows * kCandGroups * 4);
   Lo.ticket = off; off = al(off + rows * D.Hkv * (size_t)P.nhc * 4);
   Lo.cnt = off;    off = al(off + rows * (size_t)P.nch * 4);
   Lo.cand = off;   off = al(off + rows * (size_t)P.cand_cap * 8);
-  Lo.part = off;   off = al(off + rows * D.Hq * (size_t)P.S * (D.d + 2) * 4);
+  Lo.part = off;   off = al(off + rows * D.Hq * (size_t)P.S * (D.d + 4) * 4);
   Lo.total = off;
   return Lo;
 }
@@ -987,8 +1141,8 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   a.rowtag = (uint64_t*)(w + Lo.rowtag);
   a.hist0 = (uint32_t*)(w + Lo.hist0);
   a.hist1 = (uint32_t*)(w + Lo.hist1);
-  a.cand_n = (uint32_t*)(w + Lo.cand_n);
   a.ticket = (uint32_t*)(w + Lo.ticket);
+  a.cand_n = (uint32_t*)(w + Lo.cand_n);
   a.cnt = (uint32_t*)(w + Lo.cnt);
   a.cand = (uint64_t*)(w + Lo.cand);
   a.part = (float*)(w + Lo.part);
