@@ -154,6 +154,9 @@ EDGE = [
     ("decode_fp32_idx32", _w(3, 2, 9000, 4, 2, 64, 32, 333, dt="fp32")),
     ("decode_mixed_route", _w(4, 1, 12000, 8, 2, 128, 64, 500, route_p=0.5, seed=3)),
     ("decode_4_rows_long_ctx", _w(2, 4, 600000, 4, 1, 64, 64, 2048)),
+    # dense-route heads over several 128-row tiles, ragged last tile and step
+    ("mixed_route_3_tiles", _w(1, 300, 300, 8, 2, 128, 64, 48, route_p=0.5, seed=7)),
+    ("mixed_route_d64_chunk", _w(2, 200, 461, 4, 1, 64, 32, 40, route_p=0.4, seed=9)),
 ]
 
 
@@ -163,7 +166,7 @@ def test_edge_shapes(name, w, use_gate, announce):
     x = synth.make_inputs(w)
     announce(f"fused_forward {name} gate={use_gate} {w}")
     out, idx = run_fused(w, x, use_gate=use_gate)
-    rows = list(range(w.n_q)) if w.n_q <= 80 else synth.sample_rows(w, 40).tolist()
+    rows = list(range(w.n_q)) if w.n_q <= 320 else synth.sample_rows(w, 40).tolist()
     check_rows(w, x, out, idx, rows=rows, use_gate=use_gate)
 
 

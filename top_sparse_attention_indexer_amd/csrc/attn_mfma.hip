@@ -80,7 +80,8 @@ struct MfmaArgs {
   float* out;
   int B, N, L, Hq, Hkv, K;
   int n0, R;          // query rows [n0, n0 + R) of each sequence
-  int qtiles;         // dense query tiles of 64 rows per (b, h)
+  int qtiles;         // dense query tiles of DROWS rows per (b, h); 0 = no dense work
+  int do_sparse;      // sparse tokens carried by this launch
   float scale_log2;
 };
 
@@ -176,13 +177,191 @@ __device__ __forceinline__ void finish_col(ColState<HD>& st, const MfmaArgs& a, 
   }
 }
 
+
+// Dense query tile: 128 query rows of one (sequence, head), 32 per wave as two
+// 16-column tiles, against 64-key steps of the causal prefix.  The key and
+// value tiles of a step are double-buffered in LDS: the global loads of step
+// s + 1 are issued before the MFMAs of step s and written to the other buffer
+// afterwards, so one barrier per step suffices.  Both column tiles share
+// every K operand read and every transposed V^T read.
+constexpr int DROWS = 128;       // query rows per dense tile
+constexpr int DKEYS = 64;        // keys per dense step
+constexpr int kDenseLds = 2 * DKEYS * KSTR + 2 * DKEYS * VSTR;
+
 template <int HD>
-__global__ __launch_bounds__(MT) void k_attn_mfma(MfmaArgs a) {
+__device__ void dense_tile(const MfmaArgs& a, int b, int h, int tile, char* smem) {
   constexpr int T = HD / 32;
-  // sparse: per-wave value tile + the token's index row; dense: shared tiles
-  __shared__ __attribute__((aligned(16))) char vt[4][32 * VSTR];
-  __shared__ __attribute__((aligned(16))) char kt[32 * KSTR];
-  __shared__ int ilist[2048];
+  constexpr int CPR = HD / 8;                    // 16-byte chunks per row
+  constexpr int NLD = DKEYS * CPR / MT;          // chunks per thread per tile
+  char* kbuf0 = smem;
+  char* vbuf0 = smem + 2 * DKEYS * KSTR;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, i = lane & 15;
+  const int g = h / (a.Hq / a.Hkv);
+  const int rbase = tile * DROWS;
+  const int off = a.L - a.N + a.n0;              // position of local row 0
+  const int rlast = min(a.R - 1, rbase + DROWS - 1);
+  const int pmax = off + rlast;                  // last key any row of the tile sees
+  const int wlast = min(a.R - 1, rbase + w * 32 + 31);
+  const int pmax_wave = off + wlast;
+  bf16x8 qb[2][T];
+  int prow[2];
+  bool rvalid[2];
+  size_t orow[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = rbase + w * 32 + c * 16 + i;
+    rvalid[c] = r < a.R;
+    const int n = a.n0 + (rvalid[c] ? r : 0);
+    prow[c] = rvalid[c] ? off + r : -1;
+    orow[c] = ((size_t)b * a.N + n) * a.Hq + h;
+    const bf16_bits* qr = a.q + orow[c] * HD;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      uint4 u = rvalid[c] ? *reinterpret_cast<const uint4*>(qr + q * (HD / 4) + t * 8)
+                          : make_uint4(0, 0, 0, 0);
+      qb[c][t] = as_bf16x8(u);
+    }
+  }
+  ColState<HD> st[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    st[c].m = -INFINITY;
+    st[c].l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) st[c].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const size_t rstride = (size_t)a.Hkv * HD;
+  uint4 kreg[NLD], vreg[NLD];
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int x = 0; x < NLD; ++x) {
+      const int cidx = x * MT + threadIdx.x;
+      const int r = cidx / CPR, cc = cidx - r * CPR;
+      const int j = j0 + r;
+      kreg[x] = make_uint4(0, 0, 0, 0);
+      vreg[x] = make_uint4(0, 0, 0, 0);
+      if (j <= pmax) {
+        kreg[x] = *reinterpret_cast<const uint4*>(kbase + (size_t)j * rstride + cc * 8);
+        vreg[x] = *reinterpret_cast<const uint4*>(vbase + (size_t)j * rstride + cc * 8);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+    char* kt = kbuf0 + buf * DKEYS * KSTR;
+    char* vt = vbuf0 + buf * DKEYS * VSTR;
+#pragma unroll
+    for (int x = 0; x < NLD; ++x) {
+      const int cidx = x * MT + threadIdx.x;
+      const int r = cidx / CPR, cc = cidx - r * CPR;
+      *reinterpret_cast<uint4*>(kt + r * KSTR + cc * 16) = kreg[x];
+      *reinterpret_cast<uint4*>(vt + r * VSTR + cc * 16) = vreg[x];
+    }
+  };
+  const int nsteps = pmax / DKEYS + 1;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int row0 = 4 * q + (i >> 2);   // value row this lane points at (transposing read)
+  const int colb = (i & 3) * 8;
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
+    const int j0 = sidx * DKEYS;
+    const bool more = sidx + 1 < nsteps;
+    if (more) fetch(j0 + DKEYS);
+    if (j0 <= pmax_wave) {
+      const char* kt = kbuf0 + (sidx & 1) * DKEYS * KSTR;
+      const char* vt = vbuf0 + (sidx & 1) * DKEYS * VSTR;
+      // S^T: 4 blocks of 16 keys x 16 columns, for both column tiles
+      f32x4 sacc[2][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bf16x8 ka[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          ka[t] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + (u * 16 + i) * KSTR +
+                                                             (q * (HD / 4) + t * 8) * 2));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc = mfma16(ka[t], qb[c][t], acc);
+          sacc[c][u] = acc;
+        }
+      }
+      // online softmax per column; P^T packed per 32-key half
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float sv[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + u * 16 + 4 * q + r;
+            sv[u * 4 + r] = (j <= prow[c]) ? sacc[c][u][r] * a.scale_log2 : -INFINITY;
+          }
+        float mt = sv[0];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) mt = fmaxf(mt, sv[x]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mnew = fmaxf(st[c].m, mt);
+        float alpha = 1.f;
+        float pv[16];
+        if (mnew == -INFINITY) {
+#pragma unroll
+          for (int x = 0; x < 16; ++x) pv[x] = 0.f;
+        } else {
+          alpha = exp2f(st[c].m - mnew);
+#pragma unroll
+          for (int x = 0; x < 16; ++x) pv[x] = exp2f(sv[x] - mnew);
+        }
+        float ps = 0.f;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) ps += pv[x];
+        st[c].l = st[c].l * alpha + ps;
+        st[c].m = mnew;
+        // half v: keys 32v + 4q + r (block 2v) then 32v + 16 + 4q + r (block 2v + 1)
+        pb[c][0] = pack8(pv);
+        pb[c][1] = pack8(pv + 8);
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st[c].o[dt][r] *= alpha;
+      }
+      // O^T += V^T P^T for both halves; V^T read once for both column tiles
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt) {
+          const uint2 lo = lds_tr(vt, (32 * v + row0) * VSTR + dt * 32 + colb);
+          const uint2 hi = lds_tr(vt, (32 * v + 16 + row0) * VSTR + dt * 32 + colb);
+          uint4 u4;
+          u4.x = lo.x; u4.y = lo.y; u4.z = hi.x; u4.w = hi.y;
+          const bf16x8 va = as_bf16x8(u4);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) st[c].o[dt] = mfma16(va, pb[c][v], st[c].o[dt]);
+        }
+      }
+    }
+    if (more) stash((sidx + 1) & 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) finish_col<HD>(st[c], a, orow[c], rvalid[c]);
+}
+
+template <int HD>
+__global__ __launch_bounds__(MT, 2) void k_attn_mfma(MfmaArgs a) {
+  constexpr int T = HD / 32;
+  // sparse: per-wave value tile + the token's index row; dense: double-
+  // buffered key and value tiles (the two uses share the LDS)
+  constexpr int kSparseLds = 4 * 32 * VSTR + 2048 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kDenseLds > kSparseLds ? kDenseLds : kSparseLds];
+  char (*vt)[32 * VSTR] = reinterpret_cast<char (*)[32 * VSTR]>(smem);
+  int* ilist = reinterpret_cast<int*>(smem + 4 * 32 * VSTR);
   __shared__ int s_nd, s_lastv;
   __shared__ int s_pair;
 
@@ -214,77 +393,14 @@ __global__ __launch_bounds__(MT) void k_attn_mfma(MfmaArgs a) {
     }
     __syncthreads();
     const int pair = s_pair;
-    const int b = pair / a.Hq, h = pair - b * a.Hq, g = h / Gh;
-    const int rbase = tile * 64;                // local row within [0, R)
-    const int myrow = rbase + w * 16 + i;       // this lane's column = query row
-    const bool rvalid = myrow < a.R;
-    const int n = a.n0 + myrow;
-    const int p = a.L - a.N + n;                // last visible key of the row
-    const int rlast = min(a.R - 1, rbase + 63);
-    const int pmax = a.L - a.N + a.n0 + rlast;
-    const int pmin_wave = a.L - a.N + a.n0 + rbase + w * 16;
-    // Q^T operand (dims in the permuted order q*32 + t*8)
-    bf16x8 qb[T];
-    {
-      const bf16_bits* qr = a.q + (((size_t)b * a.N + (rvalid ? n : a.n0)) * a.Hq + h) * HD;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        uint4 u = rvalid ? *reinterpret_cast<const uint4*>(qr + q * (HD / 4) + t * 8)
-                         : make_uint4(0, 0, 0, 0);
-        qb[t] = as_bf16x8(u);
-      }
-    }
-    ColState<HD> st;
-    st.m = -INFINITY;
-    st.l = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
-    const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
-    const size_t rstride = (size_t)a.Hkv * HD;   // elements between key rows
-    char* vtile = vt[0];
-    for (int j0 = 0; j0 <= pmax; j0 += 32) {
-      // cooperative load of the K tile (row-major, 256 B rows for d = 128) and
-      // the V tile (288 B stride) into LDS
-      constexpr int CPR = HD / 8;                // 16-byte chunks per row
-      for (int cidx = threadIdx.x; cidx < 32 * CPR; cidx += MT) {
-        const int r = cidx / CPR, cc = cidx - r * CPR;
-        const int j = j0 + r;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (j <= pmax) {
-          kv = *reinterpret_cast<const uint4*>(kbase + (size_t)j * rstride + cc * 8);
-          vv = *reinterpret_cast<const uint4*>(vbase + (size_t)j * rstride + cc * 8);
-        }
-        *reinterpret_cast<uint4*>(kt + r * KSTR + cc * 16) = kv;
-        *reinterpret_cast<uint4*>(vtile + r * VSTR + cc * 16) = vv;
-      }
-      __syncthreads();
-      if (j0 <= pmin_wave + 15) {   // some row of this wave sees a key of the tile
-        uint4 ka[2][T];
-        bool kval[2][4];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int t = 0; t < T; ++t)
-            ka[u][t] = *reinterpret_cast<const uint4*>(kt + (u * 16 + i) * KSTR +
-                                                        (q * (HD / 4) + t * 8) * 2);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) kval[u][r] = rvalid && (j0 + u * 16 + 4 * q + r) <= p;
-        }
-        // A operand rows are the keys: lane (q, i) supplies key i of the half;
-        // the output row index (keys 4q + r) belongs to the column lane.
-        step_core<HD>(ka, qb, kval, vtile, a.scale_log2, st);
-      }
-      __syncthreads();
-    }
-    const size_t orow = ((size_t)b * a.N + n) * a.Hq + h;
-    finish_col<HD>(st, a, orow, rvalid);
+    const int b = pair / a.Hq, h = pair - b * a.Hq;
+    dense_tile<HD>(a, b, h, tile, smem);
     return;
   }
 
   // -------------------------------------------------------------- sparse token
   const long long sidx = item - n_dense_items;
-  if (sidx >= (long long)a.B * a.R) return;
+  if (!a.do_sparse || sidx >= (long long)a.B * a.R) return;
   const int b = (int)(sidx / a.R), r_loc = (int)(sidx - (long long)b * a.R);
   const int n = a.n0 + r_loc;
   const int p = a.L - a.N + n;
@@ -390,10 +506,12 @@ hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& aa, hipStream_t 
   a.gate = aa.gate; a.y2 = aa.y2; a.route = aa.route; a.out = aa.out;
   a.B = D.B; a.N = D.N; a.L = D.L; a.Hq = D.Hq; a.Hkv = D.Hkv; a.K = D.K;
   a.n0 = aa.n0; a.R = aa.R;
-  a.qtiles = (aa.R + 63) / 64;
+  a.qtiles = aa.skip_dense ? 0 : (aa.R + DROWS - 1) / DROWS;
+  a.do_sparse = aa.skip_sparse ? 0 : 1;
   a.scale_log2 = D.scale * kLog2e;
   const long long dense_max = aa.route ? (long long)D.B * D.Hq * a.qtiles : 0;
-  const long long blocks = dense_max + (long long)D.B * aa.R;
+  const long long blocks = dense_max + (aa.skip_sparse ? 0 : (long long)D.B * aa.R);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (D.d == 128)
     hipLaunchKernelGGL(k_attn_mfma<128>, dim3((unsigned)blocks), dim3(MT), 0, s, a);

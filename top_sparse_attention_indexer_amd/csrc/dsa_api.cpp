@@ -317,6 +317,18 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
   int32_t* idx_chunk = (int32_t*)(w + P.idx_off);
   float* part = P.part_bytes ? (float*)(w + P.part_off) : nullptr;
   hipError_t e = hipSuccess;
+  const bool mfma = !P.decode && dsa::mfma_attention_supported(D);
+  if (mfma && route && P.R < D.N) {
+    // dense-route heads need no indices: one launch over every query row
+    // (row chunks exist only for the score buffer of the sparse heads)
+    dsa::AttnArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.topk = idx_chunk; a.idx_rows_per_b = P.R; a.idx_n_base = 0;
+    a.gate = gate; a.y2 = y2; a.route = route; a.out = out;
+    a.n0 = 0; a.R = D.N;
+    a.skip_sparse = true;
+    e = dsa::launch_attention_mfma(D, a, s);
+  }
   for (int n0 = 0; n0 < D.N && e == hipSuccess; n0 += P.R) {
     const int R = std::min(P.R, D.N - n0);
     const int ncols = D.L - D.N + n0 + R;  // keys visible to the last row of the chunk
@@ -341,10 +353,12 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
     a.n0 = n0; a.R = R;
     a.splits_sparse = P.splits_sparse;
     a.splits_dense = P.splits_dense;
-    if (!P.decode && dsa::mfma_attention_supported(D))
+    if (mfma) {
+      a.skip_dense = route && P.R < D.N;   // already done above
       e = dsa::launch_attention_mfma(D, a, s);
-    else
+    } else {
       e = dsa::launch_attention(D, a, s);
+    }
   }
   return hip_status(e, "dsa_fused_forward");
 }

@@ -53,6 +53,8 @@ struct AttnArgs {
   float* part;              // partials for split keys (nullable when splits == 1)
   int n0, R;                // query rows handled: [n0, n0 + R) of each sequence
   int splits_sparse, splits_dense;
+  // MFMA attention only: which work the launch carries (both by default)
+  bool skip_dense = false, skip_sparse = false;
 };
 size_t attn_part_bytes(const Dims& D, int R, int splits);
 void attn_pick_splits(const Dims& D, int R, int& splits_sparse, int& splits_dense);
