@@ -25,53 +25,15 @@
 //     by lanes 4k + i/4.
 #include "common.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace dsa {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int MT = 256;          // threads (4 waves)
 constexpr int VSTR = 288;        // LDS row stride of a 32 x d value tile (bytes)
 constexpr int KSTR = 272;        // LDS row stride of a 32 x d key tile (bytes)
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, 16);
-  return r;
-}
-
-// float -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ bf16x8 pack8(const float* p) {
-  uint4 u;
-  u.x = bf16_rne(p[0]) | (bf16_rne(p[1]) << 16);
-  u.y = bf16_rne(p[2]) | (bf16_rne(p[3]) << 16);
-  u.z = bf16_rne(p[4]) | (bf16_rne(p[5]) << 16);
-  u.w = bf16_rne(p[6]) | (bf16_rne(p[7]) << 16);
-  return as_bf16x8(u);
-}
-
-__device__ __forceinline__ uint2 lds_tr(const char* lds_base, int byte_off) {
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16*)((__attribute__((address_space(3))) char*)lds_base + byte_off));
-  uint2 r;
-  __builtin_memcpy(&r, &v, 8);
-  return r;
-}
 
 struct MfmaArgs {
   const bf16_bits* q; const bf16_bits* k; const bf16_bits* v;

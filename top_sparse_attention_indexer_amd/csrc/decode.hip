@@ -35,6 +35,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace dsa {
 namespace {
@@ -448,6 +449,167 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
   __syncthreads();
 }
 
+
+// bf16 keys and values on MFMA: one pass of a wave covers 64 keys as four
+// blocks of 16.  S^T = K Q^T with the item's heads as the 16 columns (lane
+// column i = head i), the online softmax per column in registers, then
+// O^T += V^T P^T with V^T read from this wave's LDS value tile by the
+// transposing LDS read.  The d axis is taken in 32-dim chunks, so the four
+// lane quads of one key read 64 contiguous bytes of its row.  The four waves
+// are merged through LDS; one partial (max, sum, acc) per head is written
+// for split s.
+template <int HD>
+__device__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
+                            int e0, int e1, const int* hsel, int nh, float* lds) {
+  constexpr int T = HD / 32;
+  constexpr int NC = 16;                      // columns (heads) per item
+  constexpr int LPR = HD / 8;                 // lanes per value row (16-byte pieces)
+  constexpr int KPI = 64 / LPR;               // value rows per load instruction
+  const bf16_bits* K = (const bf16_bits*)a.k;
+  const bf16_bits* V = (const bf16_bits*)a.v;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, i = lane & 15;
+  const int p = a.L - a.N + n;
+  char* vtile = (char*)lds + w * 64 * HD * 2;  // this wave's 64 value rows
+  float* wb = lds;                             // [4][NC][HD], after the key loop
+  float* wml = lds + 16384;                    // [4][NC][2]
+  bf16x8 qb[T];
+  {
+    const bool hv = i < nh;
+    const bf16_bits* qr =
+        (const bf16_bits*)a.q + (((size_t)b * a.N + n) * a.Hq + (hv ? hsel[i] : 0)) * HD;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      qb[t] = as_bf16x8(hv ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
+                           : make_uint4(0, 0, 0, 0));
+  }
+  float m_c = -INFINITY, l_c = 0.f;
+  f32x4 o[HD / 16];
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t* lrow = (const uint32_t*)a.list + (size_t)row * a.K;
+  const bf16_bits* kseq = K + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const bf16_bits* vseq = V + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const size_t rs = (size_t)a.Hkv * HD;        // elements between token rows
+  const int ks = lane / LPR, dc = lane % LPR;
+  const int row0 = 4 * q + (i >> 2), colb = (i & 3) * 8;
+  for (int t0 = e0 + w * 64; t0 < e1; t0 += 4 * 64) {
+    int jl = -1;   // position of key t0 + lane
+    {
+      const int e = t0 + lane;
+      if (e < e1) {
+        jl = dense ? e : (int)ld_dev(lrow + e);
+        if (jl < 0 || jl > p) jl = -1;
+      }
+    }
+    const uint64_t vm = __ballot(jl >= 0);
+#pragma unroll
+    for (int m = 0; m < 64 / KPI; ++m) {
+      const int jr = __shfl(jl, m * KPI + ks, 64);
+      const bf16_bits* src = vseq + (size_t)(jr < 0 ? 0 : jr) * rs + dc * 8;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src, (__attribute__((address_space(3))) void*)(vtile + m * 1024), 16, 0, 0);
+    }
+    uint4 ka[4][T];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ju = __shfl(jl, 16 * u + i, 64);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        ka[u][t] = (ju >= 0) ? *reinterpret_cast<const uint4*>(kseq + (size_t)ju * rs + t * 32 + q * 8)
+                             : make_uint4(0, 0, 0, 0);
+    }
+    float sv[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[u][t]), qb[t], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sv[u * 4 + r] = ((vm >> (16 * u + 4 * q + r)) & 1ull) ? acc[r] * a.scale_log2 : -INFINITY;
+    }
+    float mt = sv[0];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) mt = fmaxf(mt, sv[x]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mnew = fmaxf(m_c, mt);
+    float alpha = 1.f, pv[16];
+    if (mnew == -INFINITY) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) pv[x] = 0.f;
+    } else {
+      alpha = exp2f(m_c - mnew);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) pv[x] = exp2f(sv[x] - mnew);
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) ps += pv[x];
+    l_c = l_c * alpha + ps;
+    m_c = mnew;
+    // P^T for keys 32v + 4q + r (block 2v) and 32v + 16 + 4q + r (block 2v + 1)
+    const bf16x8 pb0 = pack8(pv), pb1 = pack8(pv + 8);
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
+    __builtin_amdgcn_s_waitcnt(0);      // this wave's value tile has arrived
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) {
+        const uint2 lo = lds_tr(vtile, (32 * v + row0) * (HD * 2) + dt * 32 + colb);
+        const uint2 hi = lds_tr(vtile, (32 * v + 16 + row0) * (HD * 2) + dt * 32 + colb);
+        uint4 u4;
+        u4.x = lo.x; u4.y = lo.y; u4.z = hi.x; u4.w = hi.y;
+        o[dt] = mfma16(as_bf16x8(u4), v ? pb1 : pb0, o[dt]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);      // tile reads done before it is refilled
+    __builtin_amdgcn_wave_barrier();
+  }
+  l_c += __shfl_xor(l_c, 16, 64);
+  l_c += __shfl_xor(l_c, 32, 64);
+  __syncthreads();   // value tiles are dead; their LDS becomes the merge buffer
+  if (i < nh) {
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wb[(w * NC + i) * HD + dt * 16 + 4 * q + r] = o[dt][r];
+    if (q == 0) {
+      wml[(w * NC + i) * 2 + 0] = m_c;
+      wml[(w * NC + i) * 2 + 1] = l_c;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nh * HD; e += DT) {
+    const int hh = e / HD, c = e - hh * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, wml[(ww * NC + hh) * 2]);
+    float l = 0.f, s_acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = wml[(ww * NC + hh) * 2];
+        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        l = fmaf(f, wml[(ww * NC + hh) * 2 + 1], l);
+        s_acc = fmaf(f, wb[(ww * NC + hh) * HD + c], s_acc);
+      }
+    }
+    float* pp = a.part + (((size_t)row * a.Hq + hsel[hh]) * a.S + s) * (HD + 4);
+    st_devf(pp + 4 + c, s_acc);
+    if (c == 0) {
+      st_devf(pp + 0, M);
+      st_devf(pp + 1, l);
+    }
+  }
+  __syncthreads();
+}
+
 // Attention item `it`: (row, KV head g, key split s, head chunk hci), the
 // split index varying fastest so that the splits of one (row, KV head, head
 // chunk) run side by side.
@@ -634,9 +796,10 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
 
   // q of this workgroup's first attention item: loaded now, moved to LDS once
   // the selection below no longer needs that LDS
-  constexpr int NQ = (HCT * HD + DT - 1) / DT;
+  constexpr bool kMfma = sizeof(TQ) == 2;   // bf16 keys/values: MFMA attention
+  constexpr int NQ = kMfma ? 1 : (HCT * HD + DT - 1) / DT;
   const int items = a.B * N * a.Hkv * a.S * a.nhc;
-  const bool q_pre = (int)blockIdx.x < items;
+  const bool q_pre = !kMfma && (int)blockIdx.x < items;
   float qreg[NQ];
   if (q_pre) {
     const Item t = item_of(a, blockIdx.x);
@@ -890,12 +1053,18 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       const bool first = it == (int)blockIdx.x;   // q already in LDS
       if (ns > 0) {
         const int e0 = s * per_s, e1 = min(K, e0 + per_s);
-        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds, first);
+        if constexpr (kMfma)
+          attend_mfma<HD>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds);
+        else
+          attend<TQ, HD, HCT>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds, first);
       }
       if (nd > 0) {
         const int e0 = s * per_d, e1 = min(vis, e0 + per_d);
-        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds,
-                            first && ns == 0);
+        if constexpr (kMfma)
+          attend_mfma<HD>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds);
+        else
+          attend<TQ, HD, HCT>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds,
+                              first && ns == 0);
       }
       // ticket: the last split of this (row, g, hci) merges
       __builtin_amdgcn_s_waitcnt(0);
@@ -992,8 +1161,13 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
 
 template <typename TI, int DIDX, typename TQ, int HD>
 const void* decode_kernel(int G) {
-  if (G <= 4) return reinterpret_cast<const void*>(&k_decode<TI, DIDX, TQ, HD, 4>);
-  return reinterpret_cast<const void*>(&k_decode<TI, DIDX, TQ, HD, 8>);
+  if constexpr (sizeof(TQ) == 2) {
+    (void)G;
+    return reinterpret_cast<const void*>(&k_decode<TI, DIDX, TQ, HD, 16>);
+  } else {
+    if (G <= 4) return reinterpret_cast<const void*>(&k_decode<TI, DIDX, TQ, HD, 4>);
+    return reinterpret_cast<const void*>(&k_decode<TI, DIDX, TQ, HD, 8>);
+  }
 }
 
 template <typename TI, typename TQ, int HD>
@@ -1055,7 +1229,7 @@ bool decode_plan(const Dims& D, int grid, DecodePlan& P) {
   P.CH = (int)ch;
   P.nch = nch;
   const int G = D.Hq / D.Hkv;
-  const int hct = G <= 4 ? 4 : 8;
+  const int hct = D.qkv_bf16 ? 16 : (G <= 4 ? 4 : 8);   // heads per attention item
   P.nhc = (G + hct - 1) / hct;
   // one split per 256 keys: every split keeps the four waves of its
   // workgroup busy with one 64-key pass each
