@@ -46,7 +46,6 @@ constexpr int kLdsFloats = 16384 + 8 * 128 + 64;  // value tiles / scores + q + 
 constexpr int DMAXCH = 2048;   // max chunks per sequence
 constexpr int kMaxGrid = 4096;  // largest grid the control block is sized for
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kCoherentLoad = 16;   // cache policy of a device-coherent load (sc1)
 
 struct DecodeArgs {
   const void* q_idx; const void* k_idx; const void* q; const void* k; const void* v;
@@ -1075,66 +1074,80 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       }
       __syncthreads();
       if (res[0]) {
-        // The partials of the item's heads go straight from memory into LDS
-        // (16-byte pieces, coherent loads, no registers), together with this
-        // thread's gate and second-branch values; then each thread merges its
+        // One round of loads per 8 splits: this thread's accumulator elements
+        // (registers) and every (head, split) max and sum (to LDS), together
+        // with the gate and second-branch values; then each thread merges its
         // (head, dim) elements over the splits with a running max.
         constexpr int PS = HD + 4;                   // floats per partial
-        constexpr int CPP = PS / 4;                  // 16-byte pieces per partial
         constexpr int NE = (HCT * HD + DT - 1) / DT;
+        constexpr int MB = 8;                        // splits per round
         const int nh = ns + nd;
         const int S = a.S;
-        const int SB = max(1, min(S, 16384 / (nh * PS)));   // splits per LDS batch
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        float* mls = lds;                            // [nh][MB] (max, sum)
         float Mx[NE], Lx[NE], Ax[NE], gv[NE], yv[NE];
 #pragma unroll
         for (int k = 0; k < NE; ++k) {
-          const int e = threadIdx.x + k * DT;
-          const int hh = e / HD, cth = e - hh * HD;
-          const bool ok = e < nh * HD;
-          const int h = !ok ? 0 : (hh < ns ? hsel[0][hh] : hsel[1][hh - ns]);
-          const size_t orow = (size_t)row * a.Hq + h;
-          const bool gk = ok && a.gate;
-          gv[k] = gk ? a.gate[orow] : 1.f;
-          yv[k] = gk ? a.y2[orow * HD + cth] : 0.f;
           Mx[k] = -INFINITY;
           Lx[k] = 0.f;
           Ax[k] = 0.f;
+          gv[k] = 1.f;
+          yv[k] = 0.f;
         }
-        for (int s0 = 0; s0 < S; s0 += SB) {
-          const int sb = min(SB, S - s0);
-          const int npieces = nh * sb * CPP;
-          for (int c0 = w * 64; c0 < npieces; c0 += DT) {
-            const int ci = c0 + lane;
-            if (ci < npieces) {
-              const int hh = ci / (sb * CPP);
-              const int rem = ci - hh * sb * CPP;
-              const int sl = rem / CPP, cc = rem - sl * CPP;
-              const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
-              const float* src = a.part + (((size_t)row * a.Hq + h) * S + s0 + sl) * PS + cc * 4;
-              __builtin_amdgcn_global_load_lds(
-                  (const void*)src, (__attribute__((address_space(3))) void*)(lds + c0 * 4), 16, 0,
-                  kCoherentLoad);
+        for (int s0 = 0; s0 < S; s0 += MB) {
+          const int sb = min(MB, S - s0);
+          float av[NE][MB];
+#pragma unroll
+          for (int k = 0; k < NE; ++k) {
+            const int e = threadIdx.x + k * DT;
+            const bool ok = e < nh * HD;
+            const int hh = e / HD, cth = e - hh * HD;
+            const int h = !ok ? 0 : (hh < ns ? hsel[0][hh] : hsel[1][hh - ns]);
+            const size_t orow = (size_t)row * a.Hq + h;
+            const float* pk = a.part + (orow * S + s0) * PS + 4 + cth;
+#pragma unroll
+            for (int x = 0; x < MB; ++x) av[k][x] = (ok && x < sb) ? ld_devf(pk + (size_t)x * PS) : 0.f;
+            if (s0 == 0 && ok && a.gate) {
+              gv[k] = a.gate[orow];
+              yv[k] = a.y2[orow * HD + cth];
             }
           }
-          __builtin_amdgcn_s_waitcnt(0);
+          // every slot of [nh][MB] is written (unused splits as max -inf,
+          // sum 0) so that the reads below need no predicate
+          for (int i2 = threadIdx.x; i2 < nh * MB; i2 += DT) {
+            const int hh = i2 / MB, sl = i2 - hh * MB;
+            float mval = -INFINITY, lval = 0.f;
+            if (sl < sb) {
+              const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
+              const float* ps = a.part + (((size_t)row * a.Hq + h) * S + s0 + sl) * PS;
+              mval = ld_devf(ps);
+              lval = ld_devf(ps + 1);
+            }
+            mls[2 * i2] = mval;
+            mls[2 * i2 + 1] = lval;
+          }
           __syncthreads();
 #pragma unroll
           for (int k = 0; k < NE; ++k) {
             const int e = threadIdx.x + k * DT;
             if (e >= nh * HD) continue;
-            const int hh = e / HD, cth = e - hh * HD;
-            const float* pl = lds + hh * sb * PS;
+            const float* ml = mls + 2 * (e / HD) * MB;
+            float mv[MB], lv[MB];
+#pragma unroll
+            for (int x = 0; x < MB; ++x) {
+              mv[x] = ml[2 * x];
+              lv[x] = ml[2 * x + 1];
+            }
             float mb = Mx[k];
-            for (int sl = 0; sl < sb; ++sl) mb = fmaxf(mb, pl[sl * PS]);
+#pragma unroll
+            for (int x = 0; x < MB; ++x) mb = fmaxf(mb, mv[x]);
             if (mb == -INFINITY) continue;
             const float f0 = (Mx[k] == -INFINITY) ? 0.f : exp2f(Mx[k] - mb);
             float l = Lx[k] * f0, acc = Ax[k] * f0;
-            for (int sl = 0; sl < sb; ++sl) {
-              const float ms = pl[sl * PS];
-              const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - mb);
-              l = fmaf(f, pl[sl * PS + 1], l);
-              acc = fmaf(f, pl[sl * PS + 4 + cth], acc);
+#pragma unroll
+            for (int x = 0; x < MB; ++x) {
+              const float f = exp2f(mv[x] - mb);   // 0 for an unused or empty split
+              l = fmaf(f, lv[x], l);
+              acc = fmaf(f, av[k][x], acc);
             }
             Mx[k] = mb;
             Lx[k] = l;
