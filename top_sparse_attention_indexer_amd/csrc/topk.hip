@@ -52,6 +52,13 @@ __device__ void pick_bin(const uint32_t* hist, int nb, uint32_t kk, uint32_t* sc
   __syncthreads();
 }
 
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t x, uint32_t* scratch) {
+  uint32_t total;
+  block_excl_scan<NT>(x, scratch, total);
+  return total;
+}
+
 // ---------------------------------------------------------------- one row per workgroup
 constexpr int RT = 1024;
 
@@ -109,6 +116,191 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ scor
     if (sel && base_sel + pos < (uint32_t)K) o[base_sel + pos] = j;
     base_tie += tie_tot;
     base_sel += sel_tot;
+  }
+}
+
+// ------------------------------------------------ one row per workgroup, row in registers
+// Rows of at most NT * E scores: each thread owns E consecutive positions.
+// The keys are read with vector loads in chunks of EC per thread; when the
+// row is one chunk (E <= 32) it is read once and every pass works from
+// registers, otherwise each pass re-reads its chunks (one batch of loads per
+// chunk, from cache).  The three digit levels histogram the keys in LDS and
+// the ordered write needs one block scan, since positions are contiguous per
+// thread.  The first-level histogram is kept in four copies (by wave) so that
+// fewer waves contend for one bin.
+constexpr int kCopies = 4;
+
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void k_topk_rows_reg(const float* __restrict__ scores, size_t ld,
+                                                      int N, int L, int K, int n0, int R,
+                                                      int32_t* __restrict__ topk,
+                                                      int idx_rows_per_b, int idx_n_base,
+                                                      const uint8_t* __restrict__ route, int Hq) {
+  constexpr int EC = E < 32 ? E : 32;   // keys per chunk
+  constexpr int NCH = E / EC;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int n = n0 + r;
+  int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
+  const int vis = L - N + n + 1;
+  if (!row_has_sparse(route, b, Hq)) {
+    for (int i = threadIdx.x; i < K; i += NT) o[i] = -1;
+    return;
+  }
+  if (vis <= K) {
+    for (int i = threadIdx.x; i < K; i += NT) o[i] = (i < vis) ? i : -1;
+    return;
+  }
+  __shared__ uint32_t hist[kCopies * 2048];
+  __shared__ uint32_t scratch[NT / DSA_WAVE + 1];
+  __shared__ uint32_t res[2];
+  const float* row = scores + ((size_t)b * R + r) * ld;
+  const int jt = threadIdx.x * E;   // this thread's positions [jt, jt + E)
+  uint32_t key[EC];
+  // keys of chunk c (positions jt + c * EC ..); 0 below every real key
+  auto load_keys = [&](int c) {
+    const int j0 = jt + c * EC;
+    if ((ld & 3) == 0) {
+      // whole vectors inside the row's ld columns are read unconditionally
+      // (columns past vis exist in the buffer) and masked afterwards
+#pragma unroll
+      for (int x = 0; x < EC; x += 4) {
+        const int j = j0 + x;
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j + 3 < (int)ld) f = *reinterpret_cast<const float4*>(row + j);
+        else if (j < vis)
+          for (int y = 0; y < 4; ++y) (&f.x)[y] = (j + y < vis) ? row[j + y] : 0.f;
+        key[x] = (j < vis) ? radix_key(f.x) : 0u;
+        key[x + 1] = (j + 1 < vis) ? radix_key(f.y) : 0u;
+        key[x + 2] = (j + 2 < vis) ? radix_key(f.z) : 0u;
+        key[x + 3] = (j + 3 < vis) ? radix_key(f.w) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < EC; ++x) key[x] = (j0 + x < vis) ? radix_key(row[j0 + x]) : 0u;
+    }
+  };
+  auto nvalid = [&](int c) { return max(0, min(EC, vis - (jt + c * EC))); };
+  if (NCH == 1) load_keys(0);
+  // A lower bound for the first-level bin of the K-th key from one key per
+  // thread: bins below b_lo are then left out of the histogram, which keeps
+  // the many keys far under the threshold (the crowded bins) away from the
+  // LDS atomics.  If fewer than K keys reach b_lo the bound was too high and
+  // the full histogram is built instead, so the result is exact either way.
+  for (int i = threadIdx.x; i < kCopies * 2048; i += NT) hist[i] = 0;
+  if (threadIdx.x == 0) res[0] = 0;
+  __syncthreads();
+  // samples: the first key of every thread holding positions; about
+  // 1.5 K * nsamp / vis of them are expected at or above the K-th key's bin
+  const long long nsamp = min((long long)NT, ((long long)vis + E - 1) / E);
+  const long long want = (3LL * K * nsamp) / (2LL * vis) + 8;
+  if (want < nsamp / 2) {
+    if (NCH > 1) load_keys(0);
+    if (nvalid(0) > 0) atomicAdd(&hist[2048 + (key[0] >> 21)], 1u);
+    __syncthreads();
+    pick_bin<NT>(hist + 2048, 2048, (uint32_t)want, scratch, res);
+    if (threadIdx.x < 2048 / 2) {   // clear the sample histogram for level 0
+      hist[2048 + 2 * threadIdx.x] = 0;
+      hist[2048 + 2 * threadIdx.x + 1] = 0;
+    }
+    __syncthreads();
+  }
+  uint32_t b_lo = res[0];
+  // level 0: top 11 bits of the keys in bins >= b_lo, four histogram copies
+  uint32_t nhi = 0;
+  {
+    uint32_t* hc = hist + ((threadIdx.x / DSA_WAVE) % kCopies) * 2048;
+    for (int c = 0; c < NCH; ++c) {
+      if (NCH > 1) load_keys(c);
+      const int nv = nvalid(c);
+#pragma unroll
+      for (int x = 0; x < EC; ++x)
+        if (x < nv && (key[x] >> 21) >= b_lo) {
+          atomicAdd(&hc[key[x] >> 21], 1u);
+          ++nhi;
+        }
+    }
+    if (b_lo > 0 && block_sum_u32<NT>(nhi, scratch) < (uint32_t)K) {
+      // the bound was too high: add the keys below it
+      for (int c = 0; c < NCH; ++c) {
+        if (NCH > 1) load_keys(c);
+        const int nv = nvalid(c);
+#pragma unroll
+        for (int x = 0; x < EC; ++x)
+          if (x < nv && (key[x] >> 21) < b_lo) atomicAdd(&hc[key[x] >> 21], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2048; i += NT) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) t += hist[c * 2048 + i];
+    hist[i] = t;
+  }
+  __syncthreads();
+  uint32_t kk = (uint32_t)K;
+  pick_bin<NT>(hist, 2048, kk, scratch, res);
+  const uint32_t t0 = res[0];
+  kk -= res[1];
+  __syncthreads();
+  // level 1: next 11 bits of the keys in bin t0
+  for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int c = 0; c < NCH; ++c) {
+    if (NCH > 1) load_keys(c);
+    const int nv = nvalid(c);
+#pragma unroll
+    for (int x = 0; x < EC; ++x)
+      if (x < nv && (key[x] >> 21) == t0) atomicAdd(&hist[(key[x] >> 10) & 2047u], 1u);
+  }
+  __syncthreads();
+  pick_bin<NT>(hist, 2048, kk, scratch, res);
+  const uint32_t pfx = (t0 << 11) | res[0];
+  kk -= res[1];
+  __syncthreads();
+  // level 2: last 10 bits of the keys sharing the top 22
+  for (int i = threadIdx.x; i < 1024; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int c = 0; c < NCH; ++c) {
+    if (NCH > 1) load_keys(c);
+    const int nv = nvalid(c);
+#pragma unroll
+    for (int x = 0; x < EC; ++x)
+      if (x < nv && (key[x] >> 10) == pfx) atomicAdd(&hist[key[x] & 1023u], 1u);
+  }
+  __syncthreads();
+  pick_bin<NT>(hist, 1024, kk, scratch, res);
+  const uint32_t T = (pfx << 10) | res[0];
+  kk -= res[1];   // keys equal to T still to take, lowest positions first
+  // ordered write: keys > T, and the first kk keys == T
+  uint32_t ngt = 0, neq = 0;
+  for (int c = 0; c < NCH; ++c) {
+    if (NCH > 1) load_keys(c);
+    const int nv = nvalid(c);
+#pragma unroll
+    for (int x = 0; x < EC; ++x) {
+      ngt += (x < nv && key[x] > T);
+      neq += (x < nv && key[x] == T);
+    }
+  }
+  uint32_t tot_eq;
+  const uint32_t eq_before = block_excl_scan<NT>(neq, scratch, tot_eq);
+  const uint32_t take_eq = (eq_before >= kk) ? 0u : min(neq, kk - eq_before);
+  uint32_t tot_sel;
+  uint32_t pos = block_excl_scan<NT>(ngt + take_eq, scratch, tot_sel);
+  uint32_t eq_seen = 0;
+  for (int c = 0; c < NCH; ++c) {
+    if (NCH > 1) load_keys(c);
+    const int nv = nvalid(c);
+#pragma unroll
+    for (int x = 0; x < EC; ++x) {
+      const bool v = x < nv;
+      const bool eq = v && key[x] == T;
+      const bool sel = (v && key[x] > T) || (eq && eq_seen < take_eq);
+      eq_seen += eq;
+      if (sel && pos < (uint32_t)K) o[pos] = jt + c * EC + x;
+      pos += sel;
+    }
   }
 }
 
@@ -295,8 +487,19 @@ hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n
                             int32_t* topk, int idx_rows_per_b, int idx_n_base,
                             const uint8_t* route, hipStream_t s) {
   if (D.B == 0 || R == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_rows, dim3(R, D.B), dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R,
-                     topk, idx_rows_per_b, idx_n_base, route, D.Hq);
+  // the longest row of the launch decides how many scores each thread holds
+  const long long vmax = (long long)D.L - D.N + n0 + R;
+  const dim3 grid(R, D.B);
+#define DSA_TOPK_REG(NT, E)                                                                  \
+  hipLaunchKernelGGL((k_topk_rows_reg<NT, E>), grid, dim3(NT), 0, s, scores, ld, D.N, D.L, D.K, \
+                     n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq)
+  if (vmax <= 1024LL * 8) DSA_TOPK_REG(1024, 8);
+  else if (vmax <= 1024LL * 16) DSA_TOPK_REG(1024, 16);
+  else if (vmax <= 1024LL * 32) DSA_TOPK_REG(1024, 32);
+  else
+    hipLaunchKernelGGL(k_topk_rows, grid, dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R, topk,
+                       idx_rows_per_b, idx_n_base, route, D.Hq);
+#undef DSA_TOPK_REG
   return hipGetLastError();
 }
 
