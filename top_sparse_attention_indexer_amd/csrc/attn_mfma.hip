@@ -14,8 +14,10 @@
 //   S^T [16 keys x 16 cols] = K_tile [16 x d] . Q^T [d x 16]   (two halves)
 //     K rows go straight from memory into the MFMA A operand; the 16 columns
 //     are 16 query rows of one head (dense) or the heads of one KV head
-//     (sparse).  The d axis is visited in a permuted order so that each lane
-//     reads 64 contiguous bytes of a key row; Q^T uses the same order.
+//     (sparse).  Dense tiles read K from LDS with the d axis permuted (lane
+//     quad q takes dims 32 q ..), sparse tokens read K rows from memory in
+//     plain order (the four quads of a key cover 64 contiguous bytes per
+//     load); Q^T follows the same order in each case.
 //   online softmax per column, in registers (a lane owns one column);
 //   O^T [16 dims x 16 cols] += V^T [16 dims x 32 keys] . P^T [32 keys x 16]
 //     P^T is the MFMA B operand directly from registers (keys 4q..4q+3 of
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(MT, 2) void k_attn_mfma(MfmaArgs a) {
         const bf16_bits* qr = a.q + (((size_t)b * a.N + n) * a.Hq + (myh < 0 ? 0 : myh)) * HD;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          uint4 u = (myh >= 0) ? *reinterpret_cast<const uint4*>(qr + q * (HD / 4) + t * 8)
+          uint4 u = (myh >= 0) ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
                                : make_uint4(0, 0, 0, 0);
           qb[t] = as_bf16x8(u);
         }
@@ -418,18 +420,8 @@ __global__ __launch_bounds__(MT, 2) void k_attn_mfma(MfmaArgs a) {
       const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
       for (int sidx2 = 0; sidx2 < nsteps; ++sidx2) {
         const int e0 = sidx2 * 32;
-        // value rows of the 32 keys -> this wave's LDS tile
-        constexpr int CPR = HD / 8;
-#pragma unroll
-        for (int x = 0; x < 32 * CPR / 64; ++x) {
-          const int cidx = x * 64 + lane;
-          const int r = cidx / CPR, cc = cidx - r * CPR;
-          const int j = ilist[e0 + r];
-          uint4 vv = make_uint4(0, 0, 0, 0);
-          if (j >= 0) vv = *reinterpret_cast<const uint4*>(vbase + (size_t)j * rstride + cc * 8);
-          *reinterpret_cast<uint4*>(vtile + r * VSTR + cc * 16) = vv;
-        }
-        // key rows straight into the A operand
+        // key rows straight into the A operand (the four lane quads of a key
+        // read 64 contiguous bytes), issued before the value rows
         uint4 ka[2][T];
         bool kval[2][4];
 #pragma unroll
@@ -438,10 +430,27 @@ __global__ __launch_bounds__(MT, 2) void k_attn_mfma(MfmaArgs a) {
 #pragma unroll
           for (int t = 0; t < T; ++t)
             ka[u][t] = (j >= 0) ? *reinterpret_cast<const uint4*>(kbase + (size_t)j * rstride +
-                                                                   q * (HD / 4) + t * 8)
+                                                                   t * 32 + q * 8)
                                 : make_uint4(0, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) kval[u][r] = ilist[e0 + u * 16 + 4 * q + r] >= 0;
+        }
+        // value rows of the 32 keys -> this wave's LDS tile
+        constexpr int CPR = HD / 8;
+        uint4 vv[32 * CPR / 64];
+#pragma unroll
+        for (int x = 0; x < 32 * CPR / 64; ++x) {
+          const int cidx = x * 64 + lane;
+          const int r = cidx / CPR, cc = cidx - r * CPR;
+          const int j = ilist[e0 + r];
+          vv[x] = (j >= 0) ? *reinterpret_cast<const uint4*>(vbase + (size_t)j * rstride + cc * 8)
+                           : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 32 * CPR / 64; ++x) {
+          const int cidx = x * 64 + lane;
+          const int r = cidx / CPR, cc = cidx - r * CPR;
+          *reinterpret_cast<uint4*>(vtile + r * VSTR + cc * 16) = vv[x];
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's LDS tile is complete
         __builtin_amdgcn_wave_barrier();
