@@ -216,7 +216,9 @@ def test_deterministic_repeat(announce):
 
 # --------------------------------------------------------------------------- single entry points
 @pytest.mark.parametrize("N,L,didx,dt", [(1, 5000, 64, "bf16"), (5, 777, 32, "fp32"),
-                                          (100, 333, 64, "bf16"), (64, 64, 128, "fp32")])
+                                          (100, 333, 64, "bf16"), (64, 64, 128, "fp32"),
+                                          # MFMA tiles: vector stores (L % 4 == 0), d_idx 32/128
+                                          (130, 1000, 32, "bf16"), (70, 600, 128, "bf16")])
 def test_indexer_scores_entry(N, L, didx, dt, announce):
     w = _w(2, N, L, 4, 1, 64, didx, 8, dt=dt)
     x = synth.make_inputs(w, parts=("q_idx", "k_idx"))

@@ -6,6 +6,7 @@
 // (§三, the indexer_score stage).  float32 accumulation in a fixed order.
 #include "common.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace dsa {
 namespace {
@@ -85,6 +86,81 @@ __global__ __launch_bounds__(256) void k_indexer_tiles(
   }
 }
 
+// bf16 indexer inputs on MFMA: 64 query rows x 128 keys per workgroup.  Wave
+// w takes query rows 16 w .. 16 w + 15 as the MFMA columns against eight
+// blocks of 16 keys as the MFMA rows (S^T = K Q^T, fp32 accumulation over
+// d_idx in 32-wide chunks), so each lane ends with 4 consecutive keys of one
+// query row and writes them with one 16-byte store.  The key rows of a block
+// are read as 64 contiguous bytes per key by the four lane quads.
+template <int DIDX>
+__global__ __launch_bounds__(256) void k_indexer_mfma(
+    const bf16_bits* __restrict__ q_idx, const bf16_bits* __restrict__ k_idx, int N, int L,
+    int n0, int R, int ncols, float* __restrict__ out, size_t ld, int write_masked,
+    const uint8_t* __restrict__ route, int Hq) {
+  constexpr int T = DIDX / 32;
+  constexpr int UB = T <= 2 ? 8 : 4;   // key blocks whose loads are in flight together
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * 64;
+  const int j0 = blockIdx.x * 128;
+  if (!seq_has_sparse(route, b, Hq)) return;
+  const int rows_here = min(64, R - r0);
+  const int p_last = L - N + n0 + r0 + rows_here - 1;
+  if (j0 > p_last && !write_masked) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, i = lane & 15;
+  const int r = r0 + w * 16 + i;      // this lane's query row
+  const bool rv = r < R;
+  const int p = L - N + n0 + r;
+  bf16x8 qb[T];
+  {
+    const bf16_bits* qr = q_idx + ((size_t)b * N + n0 + (rv ? r : 0)) * DIDX;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      qb[t] = as_bf16x8(rv ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
+                           : make_uint4(0, 0, 0, 0));
+  }
+  float* orow = out + ((size_t)b * R + (rv ? r : 0)) * ld;
+  const bool vec = (ld & 3) == 0;
+  const bf16_bits* kseq = k_idx + (size_t)b * L * DIDX;
+  for (int u0 = 0; u0 < 8; u0 += UB) {
+    if (j0 + 16 * u0 > p_last && !write_masked) break;
+    uint4 kb[UB][T];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int jk = j0 + 16 * (u0 + u) + i;
+      const bool kv = jk < L && jk <= p_last;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        kb[u][t] = kv ? *reinterpret_cast<const uint4*>(kseq + (size_t)jk * DIDX + t * 32 + q * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(kb[u][t]), qb[t], acc);
+      const int jj = j0 + 16 * (u0 + u) + 4 * q;   // keys jj .. jj + 3 of row r
+      if (!rv) continue;
+      if (vec && jj + 3 < ncols && (jj + 3 <= p || write_masked)) {
+        float4 v;
+        v.x = (jj <= p) ? acc[0] : -INFINITY;
+        v.y = (jj + 1 <= p) ? acc[1] : -INFINITY;
+        v.z = (jj + 2 <= p) ? acc[2] : -INFINITY;
+        v.w = (jj + 3 <= p) ? acc[3] : -INFINITY;
+        *reinterpret_cast<float4*>(orow + jj) = v;
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int j = jj + x;
+          if (j >= ncols) continue;
+          if (j <= p) orow[j] = acc[x];
+          else if (write_masked) orow[j] = -INFINITY;
+        }
+      }
+    }
+  }
+}
+
 // One thread per key; the key row is read once for all RM query rows.
 template <typename TI, int RM>
 __global__ __launch_bounds__(256) void k_indexer_scan(
@@ -148,6 +224,18 @@ hipError_t launch_indexer_tiles(const Dims& D, const void* q_idx, const void* k_
                                 int ncols, float* out, size_t ld, bool write_masked,
                                 const uint8_t* route, hipStream_t s) {
   if (D.B == 0 || R == 0 || ncols == 0) return hipSuccess;
+  if (D.idx_bf16 && (D.didx == 32 || D.didx == 64 || D.didx == 128)) {
+    const dim3 g((ncols + 127) / 128, (R + 63) / 64, D.B);
+#define DSA_IDX_MFMA(DI)                                                                       \
+  hipLaunchKernelGGL(k_indexer_mfma<DI>, g, dim3(256), 0, s, (const bf16_bits*)q_idx,           \
+                     (const bf16_bits*)k_idx, D.N, D.L, n0, R, ncols, out, ld, (int)write_masked, \
+                     route, D.Hq)
+    if (D.didx == 32) DSA_IDX_MFMA(32);
+    else if (D.didx == 64) DSA_IDX_MFMA(64);
+    else DSA_IDX_MFMA(128);
+#undef DSA_IDX_MFMA
+    return hipGetLastError();
+  }
   dim3 grid((ncols + 63) / 64, (R + 63) / 64, D.B);
   if (D.idx_bf16)
     hipLaunchKernelGGL(k_indexer_tiles<bf16_bits>, grid, dim3(256), 0, s, (const bf16_bits*)q_idx,
