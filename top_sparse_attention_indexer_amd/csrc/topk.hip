@@ -52,15 +52,47 @@ __device__ void pick_bin(const uint32_t* hist, int nb, uint32_t kk, uint32_t* sc
   __syncthreads();
 }
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t x, uint32_t* scratch) {
-  uint32_t total;
-  block_excl_scan<NT>(x, scratch, total);
-  return total;
-}
-
 // ---------------------------------------------------------------- one row per workgroup
 constexpr int RT = 1024;
+
+// Three digit passes over a row held in memory, then an ordered compaction
+// (block ranks in position order).  Used for rows the faster kernels below
+// do not take.
+__device__ void row_stream(const float* __restrict__ row, int vis, int K, int32_t* __restrict__ o,
+                           uint32_t* hist, uint32_t* scratch, uint32_t* res) {
+  uint32_t prefix = 0, mask = 0, kk = (uint32_t)K;
+  for (int lv = 0; lv < 3; ++lv) {
+    const int shift = kShift[lv], nb = kBins[lv];
+    for (int i = threadIdx.x; i < nb; i += RT) hist[i] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < vis; j += RT) {
+      const uint32_t u = radix_key(row[j]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    pick_bin<RT>(hist, nb, kk, scratch, res);
+    const uint32_t t = res[0], above = res[1];
+    prefix |= t << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    kk -= above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  uint32_t base_sel = 0, base_tie = 0;
+  for (int start = 0; start < vis; start += RT) {
+    const int j = start + threadIdx.x;
+    const uint32_t u = (j < vis) ? radix_key(row[j]) : 0u;
+    const bool gt = (j < vis) && u > T;
+    const bool eq = (j < vis) && u == T;
+    uint32_t tie_tot, sel_tot;
+    const uint32_t tie_rank = block_rank<RT>(eq, scratch, tie_tot);
+    const bool sel = gt || (eq && base_tie + tie_rank < kk);
+    const uint32_t pos = block_rank<RT>(sel, scratch, sel_tot);
+    if (sel && base_sel + pos < (uint32_t)K) o[base_sel + pos] = j;
+    base_tie += tie_tot;
+    base_sel += sel_tot;
+  }
+}
 
 __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ scores, size_t ld,
                                                   int N, int L, int K, int n0, int R,
@@ -79,227 +111,194 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ scor
     for (int i = threadIdx.x; i < K; i += RT) o[i] = (i < vis) ? i : -1;
     return;
   }
-  const float* row = scores + ((size_t)b * R + r) * ld;
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scratch[RT / DSA_WAVE + 1];
   __shared__ uint32_t res[2];
-
-  uint32_t prefix = 0, mask = 0, kk = (uint32_t)K;
-  for (int lv = 0; lv < 3; ++lv) {
-    const int shift = kShift[lv], nb = kBins[lv];
-    for (int i = threadIdx.x; i < nb; i += RT) hist[i] = 0;
-    __syncthreads();
-    for (int j = threadIdx.x; j < vis; j += RT) {
-      const uint32_t u = radix_key(row[j]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    pick_bin<RT>(hist, nb, kk, scratch, res);
-    const uint32_t t = res[0], above = res[1];
-    prefix |= t << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
-    kk -= above;
-    __syncthreads();
-  }
-
-  const uint32_t T = prefix;
-  uint32_t base_sel = 0, base_tie = 0;
-  for (int start = 0; start < vis; start += RT) {
-    const int j = start + threadIdx.x;
-    const uint32_t u = (j < vis) ? radix_key(row[j]) : 0u;
-    const bool gt = (j < vis) && u > T;
-    const bool eq = (j < vis) && u == T;
-    uint32_t tie_tot, sel_tot;
-    const uint32_t tie_rank = block_rank<RT>(eq, scratch, tie_tot);
-    const bool sel = gt || (eq && base_tie + tie_rank < kk);
-    const uint32_t pos = block_rank<RT>(sel, scratch, sel_tot);
-    if (sel && base_sel + pos < (uint32_t)K) o[base_sel + pos] = j;
-    base_tie += tie_tot;
-    base_sel += sel_tot;
-  }
+  row_stream(scores + ((size_t)b * R + r) * ld, vis, K, o, hist, scratch, res);
 }
 
-// ------------------------------------------------ one row per workgroup, row in registers
-// Rows of at most NT * E scores: each thread owns E consecutive positions.
-// The keys are read with vector loads in chunks of EC per thread; when the
-// row is one chunk (E <= 32) it is read once and every pass works from
-// registers, otherwise each pass re-reads its chunks (one batch of loads per
-// chunk, from cache).  The three digit levels histogram the keys in LDS and
-// the ordered write needs one block scan, since positions are contiguous per
-// thread.  The first-level histogram is kept in four copies (by wave) so that
-// fewer waves contend for one bin.
-constexpr int kCopies = 4;
+// ------------------------------------------------ one row per workgroup, one read of the row
+// A sample of one key per thread (positions spread over the row) gives a
+// lower bound b_lo for the first-level bin of the K-th key, set so that about
+// 1.5 K keys are expected at or above it.  One coalesced pass then histograms
+// those keys and appends them (key, position) to a candidate list in LDS
+// (one LDS atomic per wave and load for the slots).  The three digit levels
+// run on the list; the selected positions go to two bitmaps (keys above T,
+// keys equal to T) that are read in position order with one block scan for
+// each, the first kk keys equal to T being taken.  A list that overflows, or
+// that holds fewer than K keys (bound too high), sends the row to the
+// multi-pass path, so the result is exact either way.
+constexpr int kCandCap = 8192;          // candidates held in LDS
+constexpr int kMaxWords = 2048;         // bitmap words: rows up to 65536 positions
 
-template <int NT, int E>
-__global__ __launch_bounds__(NT) void k_topk_rows_reg(const float* __restrict__ scores, size_t ld,
-                                                      int N, int L, int K, int n0, int R,
-                                                      int32_t* __restrict__ topk,
-                                                      int idx_rows_per_b, int idx_n_base,
-                                                      const uint8_t* __restrict__ route, int Hq) {
-  constexpr int EC = E < 32 ? E : 32;   // keys per chunk
-  constexpr int NCH = E / EC;
+__global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scores, size_t ld,
+                                                  int N, int L, int K, int n0, int R,
+                                                  int32_t* __restrict__ topk, int idx_rows_per_b,
+                                                  int idx_n_base, const uint8_t* __restrict__ route,
+                                                  int Hq) {
   const int r = blockIdx.x, b = blockIdx.y;
   const int n = n0 + r;
   int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
   const int vis = L - N + n + 1;
   if (!row_has_sparse(route, b, Hq)) {
-    for (int i = threadIdx.x; i < K; i += NT) o[i] = -1;
+    for (int i = threadIdx.x; i < K; i += RT) o[i] = -1;
     return;
   }
   if (vis <= K) {
-    for (int i = threadIdx.x; i < K; i += NT) o[i] = (i < vis) ? i : -1;
+    for (int i = threadIdx.x; i < K; i += RT) o[i] = (i < vis) ? i : -1;
     return;
   }
-  __shared__ uint32_t hist[kCopies * 2048];
-  __shared__ uint32_t scratch[NT / DSA_WAVE + 1];
-  __shared__ uint32_t res[2];
   const float* row = scores + ((size_t)b * R + r) * ld;
-  const int jt = threadIdx.x * E;   // this thread's positions [jt, jt + E)
-  uint32_t key[EC];
-  // keys of chunk c (positions jt + c * EC ..); 0 below every real key
-  auto load_keys = [&](int c) {
-    const int j0 = jt + c * EC;
-    if ((ld & 3) == 0) {
-      // whole vectors inside the row's ld columns are read unconditionally
-      // (columns past vis exist in the buffer) and masked afterwards
+  __shared__ uint32_t hist[2048];
+  __shared__ uint64_t cand[kCandCap];
+  __shared__ uint32_t bm_gt[kMaxWords], bm_eq[kMaxWords];
+  __shared__ uint32_t scratch[RT / DSA_WAVE + 1];
+  __shared__ uint32_t res[3];
+  const int lane = threadIdx.x & (DSA_WAVE - 1);
+  // bound from the sample
+  for (int i = threadIdx.x; i < 2048; i += RT) hist[i] = 0;
+  if (threadIdx.x == 0) {
+    res[0] = 0;
+    res[2] = 0;   // candidate count
+  }
+  __syncthreads();
+  uint32_t b_lo = 0;
+  const long long want = (3LL * K * RT) / (2LL * vis) + 8;
+  if (want < RT / 2) {
+    const int j = (int)(((long long)threadIdx.x * vis) / RT);
+    atomicAdd(&hist[radix_key(row[j]) >> 21], 1u);
+    __syncthreads();
+    pick_bin<RT>(hist, 2048, (uint32_t)want, scratch, res);
+    b_lo = res[0];
+    for (int i = threadIdx.x; i < 2048; i += RT) hist[i] = 0;
+  }
+  const int nwords = (vis + 31) / 32;
+  for (int i = threadIdx.x; i < nwords; i += RT) {
+    bm_gt[i] = 0;
+    bm_eq[i] = 0;
+  }
+  __syncthreads();
+  // one pass: first-level histogram of the keys >= b_lo, and the list.  A
+  // round of loads is counted first, so that the list slots cost one wave
+  // scan and one LDS atomic per wave and round.
+  auto append = [&](const uint32_t* u, const int* jv, int cnt_n) {
+    uint32_t mine = 0;
+    for (int x = 0; x < cnt_n; ++x) mine += (jv[x] < vis && (u[x] >> 21) >= b_lo);
+    const uint32_t incl = wave_incl_scan(mine);
+    uint32_t base = 0;
+    if (lane == DSA_WAVE - 1 && incl) base = atomicAdd(&res[2], incl);
+    base = __shfl(base, DSA_WAVE - 1, DSA_WAVE);
+    uint32_t slot = base + incl - mine;
+    for (int x = 0; x < cnt_n; ++x) {
+      if (jv[x] < vis && (u[x] >> 21) >= b_lo) {
+        atomicAdd(&hist[u[x] >> 21], 1u);
+        if (slot < (uint32_t)kCandCap) cand[slot] = ((uint64_t)u[x] << 32) | (uint32_t)jv[x];
+        ++slot;
+      }
+    }
+  };
+  if ((ld & 3) == 0) {
+    // 16-byte loads, four per thread in flight (16384 positions per round);
+    // whole vectors inside the row's ld columns are read unconditionally
+    for (int j0 = 0; j0 < vis; j0 += RT * 16) {
+      uint32_t u[16];
+      int jv[16];
 #pragma unroll
-      for (int x = 0; x < EC; x += 4) {
-        const int j = j0 + x;
+      for (int x = 0; x < 4; ++x) {
+        const int j = j0 + (x * RT + threadIdx.x) * 4;
         float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
         if (j + 3 < (int)ld) f = *reinterpret_cast<const float4*>(row + j);
         else if (j < vis)
           for (int y = 0; y < 4; ++y) (&f.x)[y] = (j + y < vis) ? row[j + y] : 0.f;
-        key[x] = (j < vis) ? radix_key(f.x) : 0u;
-        key[x + 1] = (j + 1 < vis) ? radix_key(f.y) : 0u;
-        key[x + 2] = (j + 2 < vis) ? radix_key(f.z) : 0u;
-        key[x + 3] = (j + 3 < vis) ? radix_key(f.w) : 0u;
+        u[4 * x] = radix_key(f.x); u[4 * x + 1] = radix_key(f.y);
+        u[4 * x + 2] = radix_key(f.z); u[4 * x + 3] = radix_key(f.w);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) jv[4 * x + y] = j + y;
       }
-    } else {
-#pragma unroll
-      for (int x = 0; x < EC; ++x) key[x] = (j0 + x < vis) ? radix_key(row[j0 + x]) : 0u;
+      append(u, jv, 16);
     }
-  };
-  auto nvalid = [&](int c) { return max(0, min(EC, vis - (jt + c * EC))); };
-  if (NCH == 1) load_keys(0);
-  // A lower bound for the first-level bin of the K-th key from one key per
-  // thread: bins below b_lo are then left out of the histogram, which keeps
-  // the many keys far under the threshold (the crowded bins) away from the
-  // LDS atomics.  If fewer than K keys reach b_lo the bound was too high and
-  // the full histogram is built instead, so the result is exact either way.
-  for (int i = threadIdx.x; i < kCopies * 2048; i += NT) hist[i] = 0;
-  if (threadIdx.x == 0) res[0] = 0;
-  __syncthreads();
-  // samples: the first key of every thread holding positions; about
-  // 1.5 K * nsamp / vis of them are expected at or above the K-th key's bin
-  const long long nsamp = min((long long)NT, ((long long)vis + E - 1) / E);
-  const long long want = (3LL * K * nsamp) / (2LL * vis) + 8;
-  if (want < nsamp / 2) {
-    if (NCH > 1) load_keys(0);
-    if (nvalid(0) > 0) atomicAdd(&hist[2048 + (key[0] >> 21)], 1u);
-    __syncthreads();
-    pick_bin<NT>(hist + 2048, 2048, (uint32_t)want, scratch, res);
-    if (threadIdx.x < 2048 / 2) {   // clear the sample histogram for level 0
-      hist[2048 + 2 * threadIdx.x] = 0;
-      hist[2048 + 2 * threadIdx.x + 1] = 0;
-    }
-    __syncthreads();
-  }
-  uint32_t b_lo = res[0];
-  // level 0: top 11 bits of the keys in bins >= b_lo, four histogram copies
-  uint32_t nhi = 0;
-  {
-    uint32_t* hc = hist + ((threadIdx.x / DSA_WAVE) % kCopies) * 2048;
-    for (int c = 0; c < NCH; ++c) {
-      if (NCH > 1) load_keys(c);
-      const int nv = nvalid(c);
+  } else {
+    for (int j0 = 0; j0 < vis; j0 += RT * 16) {
+      uint32_t u[16];
+      int jv[16];
 #pragma unroll
-      for (int x = 0; x < EC; ++x)
-        if (x < nv && (key[x] >> 21) >= b_lo) {
-          atomicAdd(&hc[key[x] >> 21], 1u);
-          ++nhi;
-        }
-    }
-    if (b_lo > 0 && block_sum_u32<NT>(nhi, scratch) < (uint32_t)K) {
-      // the bound was too high: add the keys below it
-      for (int c = 0; c < NCH; ++c) {
-        if (NCH > 1) load_keys(c);
-        const int nv = nvalid(c);
-#pragma unroll
-        for (int x = 0; x < EC; ++x)
-          if (x < nv && (key[x] >> 21) < b_lo) atomicAdd(&hc[key[x] >> 21], 1u);
+      for (int x = 0; x < 16; ++x) {
+        const int j = j0 + x * RT + threadIdx.x;
+        u[x] = (j < vis) ? radix_key(row[j]) : 0u;
+        jv[x] = j;
       }
+      append(u, jv, 16);
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 2048; i += NT) {
-    uint32_t t = 0;
-#pragma unroll
-    for (int c = 0; c < kCopies; ++c) t += hist[c * 2048 + i];
-    hist[i] = t;
+  const uint32_t nc = res[2];
+  if (nc > (uint32_t)kCandCap || nc < (uint32_t)K) {
+    __syncthreads();
+    row_stream(row, vis, K, o, hist, scratch, res);
+    return;
   }
-  __syncthreads();
+  // three digit levels on the list
   uint32_t kk = (uint32_t)K;
-  pick_bin<NT>(hist, 2048, kk, scratch, res);
+  pick_bin<RT>(hist, 2048, kk, scratch, res);
   const uint32_t t0 = res[0];
   kk -= res[1];
   __syncthreads();
-  // level 1: next 11 bits of the keys in bin t0
-  for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
+  for (int i = threadIdx.x; i < 2048; i += RT) hist[i] = 0;
   __syncthreads();
-  for (int c = 0; c < NCH; ++c) {
-    if (NCH > 1) load_keys(c);
-    const int nv = nvalid(c);
-#pragma unroll
-    for (int x = 0; x < EC; ++x)
-      if (x < nv && (key[x] >> 21) == t0) atomicAdd(&hist[(key[x] >> 10) & 2047u], 1u);
+  for (uint32_t i = threadIdx.x; i < nc; i += RT) {
+    const uint32_t u = (uint32_t)(cand[i] >> 32);
+    if ((u >> 21) == t0) atomicAdd(&hist[(u >> 10) & 2047u], 1u);
   }
   __syncthreads();
-  pick_bin<NT>(hist, 2048, kk, scratch, res);
+  pick_bin<RT>(hist, 2048, kk, scratch, res);
   const uint32_t pfx = (t0 << 11) | res[0];
   kk -= res[1];
   __syncthreads();
-  // level 2: last 10 bits of the keys sharing the top 22
-  for (int i = threadIdx.x; i < 1024; i += NT) hist[i] = 0;
+  for (int i = threadIdx.x; i < 1024; i += RT) hist[i] = 0;
   __syncthreads();
-  for (int c = 0; c < NCH; ++c) {
-    if (NCH > 1) load_keys(c);
-    const int nv = nvalid(c);
-#pragma unroll
-    for (int x = 0; x < EC; ++x)
-      if (x < nv && (key[x] >> 10) == pfx) atomicAdd(&hist[key[x] & 1023u], 1u);
+  for (uint32_t i = threadIdx.x; i < nc; i += RT) {
+    const uint32_t u = (uint32_t)(cand[i] >> 32);
+    if ((u >> 10) == pfx) atomicAdd(&hist[u & 1023u], 1u);
   }
   __syncthreads();
-  pick_bin<NT>(hist, 1024, kk, scratch, res);
+  pick_bin<RT>(hist, 1024, kk, scratch, res);
   const uint32_t T = (pfx << 10) | res[0];
   kk -= res[1];   // keys equal to T still to take, lowest positions first
-  // ordered write: keys > T, and the first kk keys == T
-  uint32_t ngt = 0, neq = 0;
-  for (int c = 0; c < NCH; ++c) {
-    if (NCH > 1) load_keys(c);
-    const int nv = nvalid(c);
-#pragma unroll
-    for (int x = 0; x < EC; ++x) {
-      ngt += (x < nv && key[x] > T);
-      neq += (x < nv && key[x] == T);
-    }
+  // selected positions into the bitmaps
+  for (uint32_t i = threadIdx.x; i < nc; i += RT) {
+    const uint64_t cd = cand[i];
+    const uint32_t u = (uint32_t)(cd >> 32), j = (uint32_t)cd;
+    if (u > T) atomicOr(&bm_gt[j >> 5], 1u << (j & 31));
+    else if (u == T) atomicOr(&bm_eq[j >> 5], 1u << (j & 31));
   }
-  uint32_t tot_eq;
-  const uint32_t eq_before = block_excl_scan<NT>(neq, scratch, tot_eq);
-  const uint32_t take_eq = (eq_before >= kk) ? 0u : min(neq, kk - eq_before);
-  uint32_t tot_sel;
-  uint32_t pos = block_excl_scan<NT>(ngt + take_eq, scratch, tot_sel);
-  uint32_t eq_seen = 0;
-  for (int c = 0; c < NCH; ++c) {
-    if (NCH > 1) load_keys(c);
-    const int nv = nvalid(c);
-#pragma unroll
-    for (int x = 0; x < EC; ++x) {
-      const bool v = x < nv;
-      const bool eq = v && key[x] == T;
-      const bool sel = (v && key[x] > T) || (eq && eq_seen < take_eq);
-      eq_seen += eq;
-      if (sel && pos < (uint32_t)K) o[pos] = jt + c * EC + x;
-      pos += sel;
+  __syncthreads();
+  // ordered write: each thread owns a contiguous run of bitmap words
+  const int wpt = (nwords + RT - 1) / RT;
+  const int w0 = threadIdx.x * wpt;
+  uint32_t ngt = 0, neq = 0;
+  for (int w = w0; w < min(nwords, w0 + wpt); ++w) {
+    ngt += __popc(bm_gt[w]);
+    neq += __popc(bm_eq[w]);
+  }
+  uint32_t tot_eq, tot_sel;
+  const uint32_t eq_before = block_excl_scan<RT>(neq, scratch, tot_eq);
+  uint32_t take = (eq_before >= kk) ? 0u : min(neq, kk - eq_before);
+  uint32_t pos = block_excl_scan<RT>(ngt + take, scratch, tot_sel);
+  for (int w = w0; w < min(nwords, w0 + wpt); ++w) {
+    uint32_t eqw = bm_eq[w];
+    uint32_t keep = 0;   // the lowest `take` bits of eqw
+    while (eqw && take) {
+      const uint32_t low = eqw & (0u - eqw);
+      keep |= low;
+      eqw ^= low;
+      --take;
+    }
+    uint32_t m = bm_gt[w] | keep;
+    while (m) {
+      const int bit = __ffs((int)m) - 1;
+      if (pos < (uint32_t)K) o[pos] = w * 32 + bit;
+      ++pos;
+      m &= m - 1;
     }
   }
 }
@@ -487,19 +486,16 @@ hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n
                             int32_t* topk, int idx_rows_per_b, int idx_n_base,
                             const uint8_t* route, hipStream_t s) {
   if (D.B == 0 || R == 0) return hipSuccess;
-  // the longest row of the launch decides how many scores each thread holds
+  // rows up to kMaxWords * 32 positions: one read of the row (candidate
+  // list in LDS); longer rows: the multi-pass kernel
   const long long vmax = (long long)D.L - D.N + n0 + R;
   const dim3 grid(R, D.B);
-#define DSA_TOPK_REG(NT, E)                                                                  \
-  hipLaunchKernelGGL((k_topk_rows_reg<NT, E>), grid, dim3(NT), 0, s, scores, ld, D.N, D.L, D.K, \
-                     n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq)
-  if (vmax <= 1024LL * 8) DSA_TOPK_REG(1024, 8);
-  else if (vmax <= 1024LL * 16) DSA_TOPK_REG(1024, 16);
-  else if (vmax <= 1024LL * 32) DSA_TOPK_REG(1024, 32);
+  if (vmax <= (long long)kMaxWords * 32)
+    hipLaunchKernelGGL(k_topk_cand, grid, dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R, topk,
+                       idx_rows_per_b, idx_n_base, route, D.Hq);
   else
     hipLaunchKernelGGL(k_topk_rows, grid, dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R, topk,
                        idx_rows_per_b, idx_n_base, route, D.Hq);
-#undef DSA_TOPK_REG
   return hipGetLastError();
 }
 
