@@ -86,9 +86,9 @@ __device__ __forceinline__ void step_core(const uint4 (&ka)[2][HD / 32], const b
 #pragma unroll
     for (int x = 0; x < 8; ++x) p[x] = 0.f;
   } else {
-    alpha = exp2f(st.m - mnew);
+    alpha = exp2_fast(st.m - mnew);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) p[x] = exp2f(s[x] - mnew);
+    for (int x = 0; x < 8; ++x) p[x] = exp2_fast(s[x] - mnew);
   }
   float ps = 0.f;
 #pragma unroll
@@ -278,9 +278,9 @@ __device__ void dense_tile(const MfmaArgs& a, int b, int h, int tile, char* smem
 #pragma unroll
           for (int x = 0; x < 16; ++x) pv[x] = 0.f;
         } else {
-          alpha = exp2f(st[c].m - mnew);
+          alpha = exp2_fast(st[c].m - mnew);
 #pragma unroll
-          for (int x = 0; x < 16; ++x) pv[x] = exp2f(sv[x] - mnew);
+          for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(sv[x] - mnew);
         }
         float ps = 0.f;
 #pragma unroll

@@ -539,9 +539,9 @@ __device__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, i
 #pragma unroll
       for (int x = 0; x < 16; ++x) pv[x] = 0.f;
     } else {
-      alpha = exp2f(m_c - mnew);
+      alpha = exp2_fast(m_c - mnew);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) pv[x] = exp2f(sv[x] - mnew);
+      for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(sv[x] - mnew);
     }
     float ps = 0.f;
 #pragma unroll
@@ -594,7 +594,7 @@ __device__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, i
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) {
         const float mw = wml[(ww * NC + hh) * 2];
-        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
         l = fmaf(f, wml[(ww * NC + hh) * 2 + 1], l);
         s_acc = fmaf(f, wb[(ww * NC + hh) * HD + c], s_acc);
       }

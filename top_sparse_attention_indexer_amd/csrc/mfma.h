@@ -46,6 +46,10 @@ __device__ __forceinline__ bf16x8 pack8(const float* p) {
   return as_bf16x8(u);
 }
 
+// 2^x with the hardware instruction alone (v_exp_f32): softmax arguments are
+// <= 0, where results below the normal range flushing to zero is harmless.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Transposing 8-byte LDS read at lds_base + byte_off (see above).
 __device__ __forceinline__ uint2 lds_tr(const char* lds_base, int byte_off) {
   const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
