@@ -30,20 +30,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return r;
 }
 
-// float -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// Eight floats -> bf16, round to nearest even (gfx950 converts two per
+// v_cvt_pk_bf16_f32; finite inputs).
 __device__ __forceinline__ bf16x8 pack8(const float* p) {
-  uint4 u;
-  u.x = bf16_rne(p[0]) | (bf16_rne(p[1]) << 16);
-  u.y = bf16_rne(p[2]) | (bf16_rne(p[3]) << 16);
-  u.z = bf16_rne(p[4]) | (bf16_rne(p[5]) << 16);
-  u.w = bf16_rne(p[6]) | (bf16_rne(p[7]) << 16);
-  return as_bf16x8(u);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)p[i];
+  return r;
 }
 
 // 2^x with the hardware instruction alone (v_exp_f32): softmax arguments are
