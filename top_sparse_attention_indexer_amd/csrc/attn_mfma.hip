@@ -77,8 +77,8 @@ __device__ __forceinline__ void step_core(const uint4 (&ka)[2][HD / 32], const b
   float mt = s[0];
 #pragma unroll
   for (int x = 1; x < 8; ++x) mt = fmaxf(mt, s[x]);
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  mt = max_xor16(mt);
+  mt = max_xor32(mt);
   const float mnew = fmaxf(st.m, mt);
   float alpha = 1.f;
   float p[8];
@@ -121,8 +121,8 @@ __device__ __forceinline__ void finish_col(ColState<HD>& st, const MfmaArgs& a, 
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4;
   float l = st.l;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_xor16(l);
+  l = sum_xor32(l);
   if (!write) return;
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
   const float g = a.gate ? a.gate[orow] : 1.f;
@@ -269,8 +269,8 @@ __device__ void dense_tile(const MfmaArgs& a, int b, int h, int tile, char* smem
         float mt = sv[0];
 #pragma unroll
         for (int x = 1; x < 16; ++x) mt = fmaxf(mt, sv[x]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = max_xor16(mt);
+        mt = max_xor32(mt);
         const float mnew = fmaxf(st[c].m, mt);
         float alpha = 1.f;
         float pv[16];

@@ -531,8 +531,8 @@ __device__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, i
     float mt = sv[0];
 #pragma unroll
     for (int x = 1; x < 16; ++x) mt = fmaxf(mt, sv[x]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = max_xor16(mt);
+    mt = max_xor32(mt);
     const float mnew = fmaxf(m_c, mt);
     float alpha = 1.f, pv[16];
     if (mnew == -INFINITY) {
@@ -570,8 +570,8 @@ __device__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, i
     __builtin_amdgcn_s_waitcnt(0);      // tile reads done before it is refilled
     __builtin_amdgcn_wave_barrier();
   }
-  l_c += __shfl_xor(l_c, 16, 64);
-  l_c += __shfl_xor(l_c, 32, 64);
+  l_c = sum_xor16(l_c);
+  l_c = sum_xor32(l_c);
   __syncthreads();   // value tiles are dead; their LDS becomes the merge buffer
   if (i < nh) {
 #pragma unroll

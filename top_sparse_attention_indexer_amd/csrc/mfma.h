@@ -43,6 +43,27 @@ __device__ __forceinline__ bf16x8 pack8(const float* p) {
 // <= 0, where results below the normal range flushing to zero is harmless.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over lane pairs l, l ^ 16 and l, l ^ 32 with the gfx950 lane
+// swaps (VALU, no LDS round trip).  With x in both operands each lane gets
+// the values of the pair's lower and upper lane, in that order, so both lanes
+// of a pair compute the same result bit for bit.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Transposing 8-byte LDS read at lds_base + byte_off (see above).
 __device__ __forceinline__ uint2 lds_tr(const char* lds_base, int byte_off) {
   const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
