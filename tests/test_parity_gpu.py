@@ -170,6 +170,39 @@ def test_edge_shapes(name, w, use_gate, announce):
     check_rows(w, x, out, idx, rows=rows, use_gate=use_gate)
 
 
+def test_long_context_prefill_chunk(announce):
+    """A 256-row prefill chunk at the end of a 300000-token context (query rows
+    over a long cache through the bottom-right causal alignment): rows wider
+    than 65536 keys take the multi-pass top-k."""
+    w = _w(1, 256, 300000, 8, 2, 128, 64, 2048, seed=21)
+    x = synth.make_inputs(w)
+    announce(f"fused_forward {w}")
+    out, idx = run_fused(w, x)
+    check_index_structure(w, idx)
+    check_rows(w, x, out, idx, rows=synth.sample_rows(w, 6).tolist())
+
+
+@pytest.mark.parametrize("N,L", [(2, 20000), (200, 3000)])
+def test_shared_key_indexer(N, L, announce):
+    """The indexer run on the attention keys: the K cache itself is passed as
+    k_idx (one KV head, d_idx = d).  The keys are integer-valued so that the
+    scores, and with them the index rows, are exact."""
+    w = _w(1, N, L, 8, 1, 128, 128, 256, seed=23)
+    x = synth.make_inputs(w)
+    x["k"] = x["k_idx"].reshape(1, L, 1, 128).astype(x["k"].dtype).copy()
+    dev = to_device(w, x)
+    p = B.problem_for(w)
+    out = torch.empty((1, N, w.h_q, w.head_dim), dtype=torch.float32, device="cuda")
+    idx = torch.full((1, N, w.top_k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    announce(f"fused_forward, k_idx = K, {w}")
+    B.dsa_fused_forward(p, dev["q_idx"], dev["k"], dev["q"], dev["k"], dev["v"], dev["gate"],
+                        dev["y2"], None, out, idx, ws)
+    torch.cuda.synchronize()
+    rows = list(range(N)) if N <= 16 else synth.sample_rows(w, 16).tolist()
+    check_rows(w, x, out, idx, rows=rows, use_route=False)
+
+
 def test_all_dense_route_skips_indexer(announce):
     w = _w(2, 50, 200, 4, 2, 128, 64, 16)
     x = synth.make_inputs(w)
