@@ -317,13 +317,20 @@ __device__ void dense_tile(const MfmaArgs& a, int b, int h, int tile, char* smem
   for (int c = 0; c < 2; ++c) finish_col<HD>(st[c], a, orow[c], rvalid[c]);
 }
 
-template <int HD>
-__global__ __launch_bounds__(MT, 2) void k_attn_mfma(MfmaArgs a) {
+// Work carried by an instantiation: dense tiles, sparse tokens, or both.  The
+// sparse-only kernel needs neither the dense path's LDS nor its registers,
+// so three of its workgroups fit on a CU instead of two.
+constexpr int kDenseWork = 1, kSparseWork = 2, kBothWork = 3;
+constexpr int kSparseLds = 4 * 32 * VSTR + 2048 * 4;
+
+template <int HD, int WORK>
+__global__ __launch_bounds__(MT, WORK == kSparseWork ? 3 : 2) void k_attn_mfma(MfmaArgs a) {
   constexpr int T = HD / 32;
   // sparse: per-wave value tile + the token's index row; dense: double-
   // buffered key and value tiles (the two uses share the LDS)
-  constexpr int kSparseLds = 4 * 32 * VSTR + 2048 * 4;
-  __shared__ __attribute__((aligned(16))) char smem[kDenseLds > kSparseLds ? kDenseLds : kSparseLds];
+  constexpr int kLds = (WORK & kDenseWork) ? (kDenseLds > kSparseLds ? kDenseLds : kSparseLds)
+                                           : kSparseLds;
+  __shared__ __attribute__((aligned(16))) char smem[kLds];
   char (*vt)[32 * VSTR] = reinterpret_cast<char (*)[32 * VSTR]>(smem);
   int* ilist = reinterpret_cast<int*>(smem + 4 * 32 * VSTR);
   __shared__ int s_nd, s_lastv;
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(MT, 2) void k_attn_mfma(MfmaArgs a) {
   const long long n_dense_items = (long long)nd * a.qtiles;
   const long long item = blockIdx.x;
 
-  if (item < n_dense_items) {
+  if ((WORK & kDenseWork) && item < n_dense_items) {
     // ------------------------------------------------------------ dense query tile
     const int tile = a.qtiles - 1 - (int)(item / nd);   // longest tiles first
     const int d_idx = (int)(item % nd);
@@ -358,13 +365,13 @@ __global__ __launch_bounds__(MT, 2) void k_attn_mfma(MfmaArgs a) {
     __syncthreads();
     const int pair = s_pair;
     const int b = pair / a.Hq, h = pair - b * a.Hq;
-    dense_tile<HD>(a, b, h, tile, smem);
+    if constexpr ((WORK & kDenseWork) != 0) dense_tile<HD>(a, b, h, tile, smem);
     return;
   }
 
   // -------------------------------------------------------------- sparse token
   const long long sidx = item - n_dense_items;
-  if (!a.do_sparse || sidx >= (long long)a.B * a.R) return;
+  if (!(WORK & kSparseWork) || !a.do_sparse || sidx >= (long long)a.B * a.R) return;
   const int b = (int)(sidx / a.R), r_loc = (int)(sidx - (long long)b * a.R);
   const int n = a.n0 + r_loc;
   const int p = a.L - a.N + n;
@@ -484,10 +491,19 @@ hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& aa, hipStream_t 
   const long long blocks = dense_max + (aa.skip_sparse ? 0 : (long long)D.B * aa.R);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (D.d == 128)
-    hipLaunchKernelGGL(k_attn_mfma<128>, dim3((unsigned)blocks), dim3(MT), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_attn_mfma<64>, dim3((unsigned)blocks), dim3(MT), 0, s, a);
+  const int work = (dense_max > 0 ? kDenseWork : 0) | (aa.skip_sparse ? 0 : kSparseWork);
+  const dim3 g((unsigned)blocks), t(MT);
+#define DSA_ATTN_MFMA(HDV)                                                                  \
+  if (work == kDenseWork) hipLaunchKernelGGL((k_attn_mfma<HDV, kDenseWork>), g, t, 0, s, a); \
+  else if (work == kSparseWork)                                                            \
+    hipLaunchKernelGGL((k_attn_mfma<HDV, kSparseWork>), g, t, 0, s, a);                     \
+  else hipLaunchKernelGGL((k_attn_mfma<HDV, kBothWork>), g, t, 0, s, a);
+  if (D.d == 128) {
+    DSA_ATTN_MFMA(128)
+  } else {
+    DSA_ATTN_MFMA(64)
+  }
+#undef DSA_ATTN_MFMA
   return hipGetLastError();
 }
 
