@@ -15,16 +15,19 @@
 //   P1  stream k_idx once: scores of the chunk's keys for all N rows into LDS;
 //       first-digit (top 11 key bits) histogram per row -> global.
 //   P2  bin t0 holding the K-th key; per chunk the count of keys above t0;
-//       keys in t0 appended to the row's candidates, their second digit
-//       (next 11 bits) histogrammed -> global.
-//   P3  each unit resolves its row's exact K-th key T (t1 from the second
-//       histogram, last digit and tie cut P* from the few candidates sharing
-//       the top 22 bits) and writes its chunk's selected positions, in order,
-//       at its prefix offset -> ascending index rows.
-//   P4  attention items (row, KV head, key split, head chunk): each wave
-//       scores 64 keys (lane = key), online softmax, PV with lane = value
-//       slice; the last split of a (row, KV head, head chunk) merges the
-//       partials and applies the gate.
+//       keys in t0 appended to the candidate region of the chunk's group
+//       (16 groups per row), their second digit (next 11 bits) histogrammed
+//       -> global.
+//   P3  each unit resolves its row's exact K-th key T and the tie cut P*
+//       (t1 from the second histogram; then a rank count, or the last digit
+//       and a radix on positions, over the few candidates sharing the top 22
+//       bits) and writes its chunk's selected positions, in order, at its
+//       prefix offset -> ascending index rows.
+//   P4  attention items (row, KV head, split of 256 keys, chunk of heads):
+//       each wave takes 64 keys per pass (bf16: MFMA with the heads as the
+//       16 columns; fp32: lane = key for scores, lane = value slice for PV),
+//       online softmax; the last split of a (row, KV head, head chunk) to
+//       finish merges the partials and applies the gate.
 #include <unistd.h>
 
 #include <chrono>

@@ -7,10 +7,13 @@
 // all of them.
 //
 // Method: radix select on the order-preserving 32-bit key of each float score
-// in three digit passes (11, 11, 10 bits) with LDS histograms, which yields the
-// exact K-th key T and the number kk of keys equal to T that are still needed.
-// An ordered compaction (wave ballots + popcounts, blocks scanned in position
-// order) then writes every key > T and the first kk keys == T, ascending.
+// in three digit levels (11, 11, 10 bits) with LDS histograms, which yields
+// the exact K-th key T and the number kk of keys equal to T that are still
+// needed; every key > T and the first kk keys == T are then written in
+// ascending position order.  Rows up to 65536 keys are read once into a
+// candidate list in LDS (k_topk_cand); wider rows, and lists that overflow,
+// take the multi-pass path (row_stream); few long rows can be split over
+// workgroups (k_split_*).
 #include "common.h"
 #include "launch.h"
 
