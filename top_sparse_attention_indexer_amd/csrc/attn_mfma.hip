@@ -46,6 +46,7 @@ struct MfmaArgs {
   int n0, R;          // query rows [n0, n0 + R) of each sequence
   int qtiles;         // dense query tiles of DROWS rows per (b, h); 0 = no dense work
   int do_sparse;      // sparse tokens carried by this launch
+  int sgpl;           // sparse tokens: KV heads per item (a divisor of Hkv)
   float scale_log2;
 };
 
@@ -371,8 +372,13 @@ __global__ __launch_bounds__(MT, WORK == kSparseWork ? 3 : 2) void k_attn_mfma(M
 
   // -------------------------------------------------------------- sparse token
   const long long sidx = item - n_dense_items;
-  if (!(WORK & kSparseWork) || !a.do_sparse || sidx >= (long long)a.B * a.R) return;
-  const int b = (int)(sidx / a.R), r_loc = (int)(sidx - (long long)b * a.R);
+  // sparse items in (sequence, block of sgpl KV heads, token) order: the
+  // workgroups resident at one time gather from one or two blocks of K/V
+  const int nblk = a.Hkv / a.sgpl;
+  if (!(WORK & kSparseWork) || !a.do_sparse || sidx >= (long long)a.B * nblk * a.R) return;
+  const int b = (int)(sidx / ((long long)nblk * a.R));
+  const int rem = (int)(sidx - (long long)b * nblk * a.R);
+  const int gblk = rem / a.R, r_loc = rem - gblk * a.R;
   const int n = a.n0 + r_loc;
   const int p = a.L - a.N + n;
   // index row into LDS; the last valid entry bounds the loop
@@ -394,10 +400,10 @@ __global__ __launch_bounds__(MT, WORK == kSparseWork ? 3 : 2) void k_attn_mfma(M
   const size_t rstride = (size_t)a.Hkv * HD;
   // (KV head, 16-head chunk) pairs spread over the four waves
   const int nhc = (Gh + 15) / 16;
-  for (int pi = w; pi < a.Hkv * nhc; pi += 4) {
-    const int g = pi / nhc;
+  for (int pi = w; pi < a.sgpl * nhc; pi += 4) {
+    const int g = gblk * a.sgpl + pi / nhc;
     {
-      const int hc = (pi - g * nhc) * 16;
+      const int hc = (pi % nhc) * 16;
       int myh = -1, cnt = 0;
       for (int x = hc; x < min(Gh, hc + 16); ++x) {
         const int h = g * Gh + x;
@@ -486,9 +492,12 @@ hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& aa, hipStream_t 
   a.n0 = aa.n0; a.R = aa.R;
   a.qtiles = aa.skip_dense ? 0 : (aa.R + DROWS - 1) / DROWS;
   a.do_sparse = aa.skip_sparse ? 0 : 1;
+  a.sgpl = (aa.sparse_heads_per_item > 0 && D.Hkv % aa.sparse_heads_per_item == 0)
+               ? aa.sparse_heads_per_item : D.Hkv;
   a.scale_log2 = D.scale * kLog2e;
   const long long dense_max = aa.route ? (long long)D.B * D.Hq * a.qtiles : 0;
-  const long long blocks = dense_max + (aa.skip_sparse ? 0 : (long long)D.B * aa.R);
+  const long long blocks =
+      dense_max + (aa.skip_sparse ? 0 : (long long)D.B * (D.Hkv / a.sgpl) * aa.R);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int work = (dense_max > 0 ? kDenseWork : 0) | (aa.skip_sparse ? 0 : kSparseWork);

@@ -96,6 +96,19 @@ struct Plan {
   size_t total = 0;
 };
 
+// KV heads per sparse attention item: the largest divisor of Hkv whose K/V
+// for one sequence stays within kGatherBudget (the 256 MB Infinity Cache has
+// to hold what the resident workgroups gather); all heads when one sequence's
+// whole K/V fits.
+constexpr size_t kGatherBudget = size_t(160) << 20;
+int sparse_heads_per_item(const dsa::Dims& D) {
+  const size_t per_head = (size_t)D.L * D.d * (D.qkv_bf16 ? 2 : 4) * 2;
+  int best = 1;
+  for (int g = 1; g <= D.Hkv; ++g)
+    if (D.Hkv % g == 0 && (size_t)g * per_head <= kGatherBudget) best = g;
+  return best;
+}
+
 int prefill_chunk_rows(const dsa::Dims& D) {
   size_t per_row = (size_t)D.B * D.L;
   size_t r = std::max<size_t>(64, kScoreBudget / std::max<size_t>(per_row, 1));
@@ -355,6 +368,7 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
     a.splits_dense = P.splits_dense;
     if (mfma) {
       a.skip_dense = route && P.R < D.N;   // already done above
+      a.sparse_heads_per_item = sparse_heads_per_item(D);
       e = dsa::launch_attention_mfma(D, a, s);
     } else {
       e = dsa::launch_attention(D, a, s);

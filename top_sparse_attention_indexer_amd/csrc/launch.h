@@ -53,8 +53,12 @@ struct AttnArgs {
   float* part;              // partials for split keys (nullable when splits == 1)
   int n0, R;                // query rows handled: [n0, n0 + R) of each sequence
   int splits_sparse, splits_dense;
-  // MFMA attention only: which work the launch carries (both by default)
+  // MFMA attention only: which work the launch carries (both by default),
+  // and how many KV heads one sparse item takes (0: all).  Items run in
+  // (sequence, block of KV heads, token) order, so fewer heads per item keep
+  // the K/V that the resident workgroups gather cache-sized.
   bool skip_dense = false, skip_sparse = false;
+  int sparse_heads_per_item = 0;
 };
 size_t attn_part_bytes(const Dims& D, int R, int splits);
 void attn_pick_splits(const Dims& D, int R, int& splits_sparse, int& splits_dense);
