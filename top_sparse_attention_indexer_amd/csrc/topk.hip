@@ -61,19 +61,20 @@ constexpr int RT = 1024;
 // Three digit passes over a row held in memory, then an ordered compaction
 // (block ranks in position order).  Used for rows the faster kernels below
 // do not take.
+template <int NT>
 __device__ void row_stream(const float* __restrict__ row, int vis, int K, int32_t* __restrict__ o,
                            uint32_t* hist, uint32_t* scratch, uint32_t* res) {
   uint32_t prefix = 0, mask = 0, kk = (uint32_t)K;
   for (int lv = 0; lv < 3; ++lv) {
     const int shift = kShift[lv], nb = kBins[lv];
-    for (int i = threadIdx.x; i < nb; i += RT) hist[i] = 0;
+    for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int j = threadIdx.x; j < vis; j += RT) {
+    for (int j = threadIdx.x; j < vis; j += NT) {
       const uint32_t u = radix_key(row[j]);
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
-    pick_bin<RT>(hist, nb, kk, scratch, res);
+    pick_bin<NT>(hist, nb, kk, scratch, res);
     const uint32_t t = res[0], above = res[1];
     prefix |= t << shift;
     mask |= (uint32_t)(nb - 1) << shift;
@@ -82,15 +83,15 @@ __device__ void row_stream(const float* __restrict__ row, int vis, int K, int32_
   }
   const uint32_t T = prefix;
   uint32_t base_sel = 0, base_tie = 0;
-  for (int start = 0; start < vis; start += RT) {
+  for (int start = 0; start < vis; start += NT) {
     const int j = start + threadIdx.x;
     const uint32_t u = (j < vis) ? radix_key(row[j]) : 0u;
     const bool gt = (j < vis) && u > T;
     const bool eq = (j < vis) && u == T;
     uint32_t tie_tot, sel_tot;
-    const uint32_t tie_rank = block_rank<RT>(eq, scratch, tie_tot);
+    const uint32_t tie_rank = block_rank<NT>(eq, scratch, tie_tot);
     const bool sel = gt || (eq && base_tie + tie_rank < kk);
-    const uint32_t pos = block_rank<RT>(sel, scratch, sel_tot);
+    const uint32_t pos = block_rank<NT>(sel, scratch, sel_tot);
     if (sel && base_sel + pos < (uint32_t)K) o[base_sel + pos] = j;
     base_tie += tie_tot;
     base_sel += sel_tot;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ scor
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scratch[RT / DSA_WAVE + 1];
   __shared__ uint32_t res[2];
-  row_stream(scores + ((size_t)b * R + r) * ld, vis, K, o, hist, scratch, res);
+  row_stream<RT>(scores + ((size_t)b * R + r) * ld, vis, K, o, hist, scratch, res);
 }
 
 // ------------------------------------------------ one row per workgroup, one read of the row
@@ -131,10 +132,12 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ scor
 // each, the first kk keys equal to T being taken.  A list that overflows, or
 // that holds fewer than K keys (bound too high), sends the row to the
 // multi-pass path, so the result is exact either way.
-constexpr int kCandCap = 8192;          // candidates held in LDS
+// Instantiations: rows up to 32768 keys with 512 threads and 6144 list slots
+// (two rows per CU); rows up to 65536 keys with 1024 threads and 8192 slots.
 constexpr int kMaxWords = 2048;         // bitmap words: rows up to 65536 positions
 
-__global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scores, size_t ld,
+template <int CT, int kCandCap>
+__global__ __launch_bounds__(CT) void k_topk_cand(const float* __restrict__ scores, size_t ld,
                                                   int N, int L, int K, int n0, int R,
                                                   int32_t* __restrict__ topk, int idx_rows_per_b,
                                                   int idx_n_base, const uint8_t* __restrict__ route,
@@ -144,39 +147,39 @@ __global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scor
   int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
   const int vis = L - N + n + 1;
   if (!row_has_sparse(route, b, Hq)) {
-    for (int i = threadIdx.x; i < K; i += RT) o[i] = -1;
+    for (int i = threadIdx.x; i < K; i += CT) o[i] = -1;
     return;
   }
   if (vis <= K) {
-    for (int i = threadIdx.x; i < K; i += RT) o[i] = (i < vis) ? i : -1;
+    for (int i = threadIdx.x; i < K; i += CT) o[i] = (i < vis) ? i : -1;
     return;
   }
   const float* row = scores + ((size_t)b * R + r) * ld;
   __shared__ uint32_t hist[2048];
   __shared__ uint64_t cand[kCandCap];
   __shared__ uint32_t bm_gt[kMaxWords], bm_eq[kMaxWords];
-  __shared__ uint32_t scratch[RT / DSA_WAVE + 1];
+  __shared__ uint32_t scratch[CT / DSA_WAVE + 1];
   __shared__ uint32_t res[3];
   const int lane = threadIdx.x & (DSA_WAVE - 1);
   // bound from the sample
-  for (int i = threadIdx.x; i < 2048; i += RT) hist[i] = 0;
+  for (int i = threadIdx.x; i < 2048; i += CT) hist[i] = 0;
   if (threadIdx.x == 0) {
     res[0] = 0;
     res[2] = 0;   // candidate count
   }
   __syncthreads();
   uint32_t b_lo = 0;
-  const long long want = (3LL * K * RT) / (2LL * vis) + 8;
-  if (want < RT / 2) {
-    const int j = (int)(((long long)threadIdx.x * vis) / RT);
+  const long long want = (3LL * K * CT) / (2LL * vis) + 8;
+  if (want < CT / 2) {
+    const int j = (int)(((long long)threadIdx.x * vis) / CT);
     atomicAdd(&hist[radix_key(row[j]) >> 21], 1u);
     __syncthreads();
-    pick_bin<RT>(hist, 2048, (uint32_t)want, scratch, res);
+    pick_bin<CT>(hist, 2048, (uint32_t)want, scratch, res);
     b_lo = res[0];
-    for (int i = threadIdx.x; i < 2048; i += RT) hist[i] = 0;
+    for (int i = threadIdx.x; i < 2048; i += CT) hist[i] = 0;
   }
   const int nwords = (vis + 31) / 32;
-  for (int i = threadIdx.x; i < nwords; i += RT) {
+  for (int i = threadIdx.x; i < nwords; i += CT) {
     bm_gt[i] = 0;
     bm_eq[i] = 0;
   }
@@ -203,12 +206,12 @@ __global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scor
   if ((ld & 3) == 0) {
     // 16-byte loads, four per thread in flight (16384 positions per round);
     // whole vectors inside the row's ld columns are read unconditionally
-    for (int j0 = 0; j0 < vis; j0 += RT * 16) {
+    for (int j0 = 0; j0 < vis; j0 += CT * 16) {
       uint32_t u[16];
       int jv[16];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const int j = j0 + (x * RT + threadIdx.x) * 4;
+        const int j = j0 + (x * CT + threadIdx.x) * 4;
         float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
         if (j + 3 < (int)ld) f = *reinterpret_cast<const float4*>(row + j);
         else if (j < vis)
@@ -221,12 +224,12 @@ __global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scor
       append(u, jv, 16);
     }
   } else {
-    for (int j0 = 0; j0 < vis; j0 += RT * 16) {
+    for (int j0 = 0; j0 < vis; j0 += CT * 16) {
       uint32_t u[16];
       int jv[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int j = j0 + x * RT + threadIdx.x;
+        const int j = j0 + x * CT + threadIdx.x;
         u[x] = (j < vis) ? radix_key(row[j]) : 0u;
         jv[x] = j;
       }
@@ -237,38 +240,38 @@ __global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scor
   const uint32_t nc = res[2];
   if (nc > (uint32_t)kCandCap || nc < (uint32_t)K) {
     __syncthreads();
-    row_stream(row, vis, K, o, hist, scratch, res);
+    row_stream<CT>(row, vis, K, o, hist, scratch, res);
     return;
   }
   // three digit levels on the list
   uint32_t kk = (uint32_t)K;
-  pick_bin<RT>(hist, 2048, kk, scratch, res);
+  pick_bin<CT>(hist, 2048, kk, scratch, res);
   const uint32_t t0 = res[0];
   kk -= res[1];
   __syncthreads();
-  for (int i = threadIdx.x; i < 2048; i += RT) hist[i] = 0;
+  for (int i = threadIdx.x; i < 2048; i += CT) hist[i] = 0;
   __syncthreads();
-  for (uint32_t i = threadIdx.x; i < nc; i += RT) {
+  for (uint32_t i = threadIdx.x; i < nc; i += CT) {
     const uint32_t u = (uint32_t)(cand[i] >> 32);
     if ((u >> 21) == t0) atomicAdd(&hist[(u >> 10) & 2047u], 1u);
   }
   __syncthreads();
-  pick_bin<RT>(hist, 2048, kk, scratch, res);
+  pick_bin<CT>(hist, 2048, kk, scratch, res);
   const uint32_t pfx = (t0 << 11) | res[0];
   kk -= res[1];
   __syncthreads();
-  for (int i = threadIdx.x; i < 1024; i += RT) hist[i] = 0;
+  for (int i = threadIdx.x; i < 1024; i += CT) hist[i] = 0;
   __syncthreads();
-  for (uint32_t i = threadIdx.x; i < nc; i += RT) {
+  for (uint32_t i = threadIdx.x; i < nc; i += CT) {
     const uint32_t u = (uint32_t)(cand[i] >> 32);
     if ((u >> 10) == pfx) atomicAdd(&hist[u & 1023u], 1u);
   }
   __syncthreads();
-  pick_bin<RT>(hist, 1024, kk, scratch, res);
+  pick_bin<CT>(hist, 1024, kk, scratch, res);
   const uint32_t T = (pfx << 10) | res[0];
   kk -= res[1];   // keys equal to T still to take, lowest positions first
   // selected positions into the bitmaps
-  for (uint32_t i = threadIdx.x; i < nc; i += RT) {
+  for (uint32_t i = threadIdx.x; i < nc; i += CT) {
     const uint64_t cd = cand[i];
     const uint32_t u = (uint32_t)(cd >> 32), j = (uint32_t)cd;
     if (u > T) atomicOr(&bm_gt[j >> 5], 1u << (j & 31));
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scor
   }
   __syncthreads();
   // ordered write: each thread owns a contiguous run of bitmap words
-  const int wpt = (nwords + RT - 1) / RT;
+  const int wpt = (nwords + CT - 1) / CT;
   const int w0 = threadIdx.x * wpt;
   uint32_t ngt = 0, neq = 0;
   for (int w = w0; w < min(nwords, w0 + wpt); ++w) {
@@ -284,9 +287,9 @@ __global__ __launch_bounds__(RT) void k_topk_cand(const float* __restrict__ scor
     neq += __popc(bm_eq[w]);
   }
   uint32_t tot_eq, tot_sel;
-  const uint32_t eq_before = block_excl_scan<RT>(neq, scratch, tot_eq);
+  const uint32_t eq_before = block_excl_scan<CT>(neq, scratch, tot_eq);
   uint32_t take = (eq_before >= kk) ? 0u : min(neq, kk - eq_before);
-  uint32_t pos = block_excl_scan<RT>(ngt + take, scratch, tot_sel);
+  uint32_t pos = block_excl_scan<CT>(ngt + take, scratch, tot_sel);
   for (int w = w0; w < min(nwords, w0 + wpt); ++w) {
     uint32_t eqw = bm_eq[w];
     uint32_t keep = 0;   // the lowest `take` bits of eqw
@@ -493,9 +496,12 @@ hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n
   // list in LDS); longer rows: the multi-pass kernel
   const long long vmax = (long long)D.L - D.N + n0 + R;
   const dim3 grid(R, D.B);
-  if (vmax <= (long long)kMaxWords * 32)
-    hipLaunchKernelGGL(k_topk_cand, grid, dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R, topk,
-                       idx_rows_per_b, idx_n_base, route, D.Hq);
+  if (vmax <= 32768)
+    hipLaunchKernelGGL((k_topk_cand<512, 6144>), grid, dim3(512), 0, s, scores, ld, D.N, D.L, D.K,
+                       n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq);
+  else if (vmax <= (long long)kMaxWords * 32)
+    hipLaunchKernelGGL((k_topk_cand<1024, 8192>), grid, dim3(1024), 0, s, scores, ld, D.N, D.L,
+                       D.K, n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq);
   else
     hipLaunchKernelGGL(k_topk_rows, grid, dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R, topk,
                        idx_rows_per_b, idx_n_base, route, D.Hq);
