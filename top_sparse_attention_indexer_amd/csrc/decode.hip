@@ -239,12 +239,6 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* scratch) {
   return total;
 }
 
-// 16-byte load widened to float: 8 bf16 or 4 fp32 elements.
-__device__ __forceinline__ void ld16(const bf16_bits* p, float* o) { ld8(p, o); }
-__device__ __forceinline__ void ld16(const float* p, float* o) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-}
 __device__ __forceinline__ uint4 raw16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void widen(const uint4& u, float* o, const bf16_bits*) {
   o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);

@@ -38,7 +38,6 @@ hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n
 
 // Rows split across workgroups (few, long rows).  Uses `ws` (split_topk_ws_bytes).
 size_t split_topk_ws_bytes(const Dims& D, int R);
-int split_topk_chunk();
 hipError_t launch_topk_split(const Dims& D, const float* scores, size_t ld, int n0, int R,
                              int32_t* topk, int idx_rows_per_b, int idx_n_base,
                              const uint8_t* route, void* ws, hipStream_t s);

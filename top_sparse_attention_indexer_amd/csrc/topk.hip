@@ -508,8 +508,6 @@ hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n
   return hipGetLastError();
 }
 
-int split_topk_chunk() { return SCH; }
-
 size_t split_topk_ws_bytes(const Dims& D, int R) {
   const size_t rows = (size_t)D.B * R;
   const size_t nch = ((size_t)D.L + SCH - 1) / SCH;
