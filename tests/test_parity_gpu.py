@@ -57,13 +57,13 @@ def check_rows(w, x, out, idx, rows, use_gate=True, use_route=True, batches=None
     return err
 
 
-def check_index_structure(w, idx):
+def check_index_structure(w, idx, batches=None):
     """Every row: ascending ids in [0, p], count min(K, vis), then -1 padding."""
     N, L, K = w.n_q, w.kv_len, w.top_k
     vis = torch.arange(N, device="cuda", dtype=torch.int64) + (L - N + 1)
     cnt = torch.clamp(vis, max=K)
     pos = torch.arange(K, device="cuda")
-    for b in range(w.batch):
+    for b in (range(w.batch) if batches is None else batches):
         t = idx[b].to(torch.int64)
         valid = pos[None, :] < cnt[:, None]
         assert torch.all(torch.where(valid, t >= 0, t == -1)).item()
@@ -157,6 +157,9 @@ EDGE = [
     # dense-route heads over several 128-row tiles, ragged last tile and step
     ("mixed_route_3_tiles", _w(1, 300, 300, 8, 2, 128, 64, 48, route_p=0.5, seed=7)),
     ("mixed_route_d64_chunk", _w(2, 200, 461, 4, 1, 64, 32, 40, route_p=0.4, seed=9)),
+    # single-row decode with fewer visible keys than K, and a short last chunk
+    ("decode_L_lt_K", _w(2, 1, 300, 4, 2, 64, 32, 512)),
+    ("decode_ragged_chunk", _w(5, 1, 3333, 8, 2, 128, 64, 700, seed=12)),
 ]
 
 
@@ -212,6 +215,34 @@ def test_all_dense_route_skips_indexer(announce):
     out, idx = run_fused(w, x)
     assert torch.all(idx[0] == -1).item()
     check_rows(w, x, out, idx, rows=list(range(w.n_q)))
+
+
+@pytest.mark.parametrize("kind", ["window", "all_equal", "all_dense_seq"])
+def test_decode_concentrated_top_k(kind, announce):
+    """Single-row decode where each chunk passes on only its few largest keys.
+    window: sequence 1's last 600 keys are boosted, so most of its top K sits
+    in a few chunks; all_equal: every score of sequence 1 is equal, so its K
+    lowest positions win.  Either way those chunks cannot pass on enough keys
+    and sequence 1 must take the histogram phases while sequences 0 and 2 do
+    not.  all_dense_seq: sequence 0 has only dense heads (no selection, index
+    row all -1)."""
+    w = _w(3, 1, 20000, 8, 2, 128, 64, 512, seed=13)
+    x = synth.make_inputs(w)
+    if kind == "window":
+        x["k_idx"][1, -600:, :] *= 3
+    elif kind == "all_equal":
+        x["k_idx"][1] = 1.0
+        x["q_idx"][1] = 1.0
+    else:
+        x["route"][0] = 0
+    announce(f"fused_forward decode {kind} {w}")
+    out, idx = run_fused(w, x)
+    check_index_structure(w, idx, batches=[1, 2] if kind == "all_dense_seq" else None)
+    if kind == "all_dense_seq":
+        assert torch.all(idx[0] == -1).item()
+    if kind == "all_equal":
+        assert torch.equal(idx[1, 0].cpu(), torch.arange(w.top_k, dtype=torch.int32))
+    check_rows(w, x, out, idx, rows=[0])
 
 
 def test_custom_softmax_scale(announce):

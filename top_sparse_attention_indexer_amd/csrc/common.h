@@ -46,15 +46,55 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (l == 0) ? 0ull : ((~0ull) >> (64 - l));
 }
 
+// One step of a DPP prefix pattern: op(x, x of the lane the control selects),
+// `ident` where that lane is outside the row or the row is masked off.
+#define DSA_DPP_STEP(x, ident, op, ctrl, rmask) \
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)(ident), (int)(x), ctrl, rmask, 0xf, false))
+
+// Inclusive prefix of a wave's 64 lanes under op on the DPP network: shifts
+// by 1, 2, 4 and 8 lanes within each row of 16, then lane 15 of each row
+// broadcast into rows 1 and 3 and lane 31 into rows 2 and 3.  No LDS traffic.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_dpp(uint32_t x, uint32_t ident, Op op) {
+  DSA_DPP_STEP(x, ident, op, 0x111, 0xf);   // row_shr:1
+  DSA_DPP_STEP(x, ident, op, 0x112, 0xf);   // row_shr:2
+  DSA_DPP_STEP(x, ident, op, 0x114, 0xf);   // row_shr:4
+  DSA_DPP_STEP(x, ident, op, 0x118, 0xf);   // row_shr:8
+  DSA_DPP_STEP(x, ident, op, 0x142, 0xa);   // row_bcast:15
+  DSA_DPP_STEP(x, ident, op, 0x143, 0xc);   // row_bcast:31
+  return x;
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < DSA_WAVE; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, DSA_WAVE);
-    if (l >= o) x += y;
+  return wave_incl_dpp(x, 0u, [](uint32_t p, uint32_t q) { return p + q; });
+}
+
+// Wave-wide sum, minimum, and 64-bit maximum (every lane gets the result).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  const uint32_t r = wave_incl_dpp(x, 0xffffffffu, [](uint32_t p, uint32_t q) { return min(p, q); });
+  return (uint32_t)__builtin_amdgcn_readlane((int)r, 63);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#define DSA_DPP_MAX64(ctrl, rmask)                                                              \
+  {                                                                                             \
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, rmask, 0xf, false); \
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), ctrl, rmask, 0xf, false); \
+    v = max(v, ((uint64_t)hi << 32) | lo);                                                      \
   }
-  return x;
+  DSA_DPP_MAX64(0x111, 0xf)
+  DSA_DPP_MAX64(0x112, 0xf)
+  DSA_DPP_MAX64(0x114, 0xf)
+  DSA_DPP_MAX64(0x118, 0xf)
+  DSA_DPP_MAX64(0x142, 0xa)
+  DSA_DPP_MAX64(0x143, 0xc)
+#undef DSA_DPP_MAX64
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float wave_max(float x) {

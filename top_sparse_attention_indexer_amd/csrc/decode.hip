@@ -10,24 +10,36 @@
 //
 // Every workgroup owns one chunk of one sequence's keys (its "unit") for the
 // whole launch.  The grid is sized to what the device holds at once (from the
-// occupancy query) and phases are separated by a two-level grid barrier whose
-// wait is bounded.
-//   P1  stream k_idx once: scores of the chunk's keys for all N rows into LDS;
-//       first-digit (top 11 key bits) histogram per row -> global.
-//   P2  bin t0 holding the K-th key; per chunk the count of keys above t0;
+// occupancy query).  All data that workgroups exchange belongs to one
+// sequence, so the phases are separated by barriers of the sequence's units
+// only (two levels, every wait bounded).
+//   P1  stream k_idx once: scores of the chunk's keys for all N rows into LDS.
+// Single-row sequences (N == 1), when the LDS holds every chunk's candidates:
+//   C1  each chunk passes on its M largest keys under (key descending,
+//       position ascending), as order values key << 32 | ~position in
+//       position order, and its (M+1)-th value.
+//   C2  after one barrier, every unit with an attention item loads the row's
+//       candidates, finds their K-th largest value cK and checks that cK is
+//       above every chunk's (M+1)-th value; if so the index list is the
+//       candidates at or above cK in position order, built in LDS, and the
+//       unit goes straight to its attention items.  Otherwise the sequence
+//       takes the histogram phases below.
+// Histogram phases (N > 1, or the fallback above):
+//   H1  first-digit (top 11 key bits) histogram per row -> global.
+//   H2  bin t0 holding the K-th key; per chunk the count of keys above t0;
 //       keys in t0 appended to the candidate region of the chunk's group
-//       (16 groups per row), their second digit (next 11 bits) histogrammed
-//       -> global.
-//   P3  each unit resolves its row's exact K-th key T and the tie cut P*
+//       (16 groups per row), their second digit (next 11 bits) histogrammed.
+//   H3  each unit resolves its row's exact K-th key T and the tie cut P*
 //       (t1 from the second histogram; then a rank count, or the last digit
 //       and a radix on positions, over the few candidates sharing the top 22
 //       bits) and writes its chunk's selected positions, in order, at its
 //       prefix offset -> ascending index rows.
-//   P4  attention items (row, KV head, split of 256 keys, chunk of heads):
-//       each wave takes 64 keys per pass (bf16: MFMA with the heads as the
-//       16 columns; fp32: lane = key for scores, lane = value slice for PV),
-//       online softmax; the last split of a (row, KV head, head chunk) to
-//       finish merges the partials and applies the gate.
+//   Attention items (row, KV head, split of 256 keys, chunk of heads), taken
+//       by the units of the item's sequence: each wave takes 64 keys per pass
+//       (bf16: MFMA with the heads as the 16 columns; fp32: lane = key for
+//       scores, lane = value slice for PV), online softmax; the last split
+//       of a (row, KV head, head chunk) to finish merges the partials and
+//       applies the gate.
 #include <unistd.h>
 
 #include <chrono>
@@ -62,7 +74,12 @@ struct DecodeArgs {
   uint32_t* cnt;     // [rows][nch] per chunk: keys above the first-digit bin t0
   uint64_t* cand;    // [rows][cand_cap] key << 32 | position, one region per group
   float* part;       // [rows][Hq][S][HD+4]: max, sum, 2 pad, accumulator
+  uint64_t* fcand;   // [rows][Cpad] each chunk's M largest order values, in position order
+  uint64_t* fbound;  // [rows][nch] each chunk's (M+1)-th largest order value (0: none)
+  uint64_t* sgslot;  // [B][ngroups][8] epoch-tagged group slots of the sequence barriers
+  uint64_t* verdict; // [B][8] epoch-tagged: 1 = candidates hold the top K, 2 = they may not
   int B, N, L, Hq, Hkv, K, CH, nch, S, nhc, cand_cap;
+  int M, Cpad;       // candidates per chunk (0: histogram selection only), padded row size
   float scale_log2;
   uint32_t epoch;    // distinct per launch; tags every control word
 };
@@ -101,12 +118,9 @@ constexpr int kCandGroups = 16;
 // Control block of 64-bit words, each (launch epoch << 32 | value); a word
 // whose epoch is not the current launch's means "nothing yet", so the block
 // is never cleared.  Layout: [0] error word; member slots from word 8 (one
-// per workgroup, grouped 16 to two 64-byte lines); group slots after them,
-// one per 64-byte line.
-size_t ctl_words64(int grid) {
-  const size_t ng = (size_t)(grid + kBarGroup - 1) / kBarGroup;
-  return 8 + ng * kBarGroup + ng * 8;
-}
+// per workgroup).  The sequence barriers' group slots and the verdict words
+// are tagged the same way.
+size_t ctl_words64(int grid) { return 8 + (size_t)grid; }
 
 __device__ __forceinline__ bool tagged(uint64_t v, uint32_t epoch, uint32_t at_least) {
   return (uint32_t)(v >> 32) == epoch && (uint32_t)v >= at_least;
@@ -130,32 +144,38 @@ __device__ bool wait_tag(const DecodeArgs& a, const uint64_t* p, uint32_t at_lea
   return true;
 }
 
-// Two-level grid barrier without shared counters: every workgroup writes its
-// own arrival slot, the first workgroup of each group of 16 waits for its
-// members and writes the group slot, and every workgroup waits for all group
-// slots.  Each thread first waits for its own outstanding memory operations,
-// so the stores before the barrier have completed when the slot is written.
-__device__ bool grid_sync(const DecodeArgs& a, uint32_t phase, int* flag) {
+// Barrier of the units of one sequence (workgroups [b * nch, (b + 1) * nch)):
+// all data exchanged between workgroups belongs to one sequence, so no
+// workgroup waits for another sequence's.  No shared counters: every unit
+// writes its own arrival slot, the first unit of each group of 16 (counted
+// within the sequence) waits for its members and writes the group slot, and
+// every unit waits for the sequence's group slots.  Each thread first waits
+// for its own outstanding memory operations, so the stores before the
+// barrier have completed when the slot is written.
+__device__ bool seq_sync(const DecodeArgs& a, int b, uint32_t phase, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int G = gridDim.x;
-  const int ngroups = (G + kBarGroup - 1) / kBarGroup;
-  const int g = blockIdx.x / kBarGroup;
+  const int u0 = b * a.nch;
+  const int lu = (int)blockIdx.x - u0;
+  const int ngs = (a.nch + kBarGroup - 1) / kBarGroup;
+  const int gi = lu / kBarGroup;
   uint64_t* mslot = a.ctl + 8;
-  uint64_t* gslot = a.ctl + 8 + (size_t)ngroups * kBarGroup;
+  uint64_t* gslot = a.sgslot + (size_t)b * ngs * 8;
   const uint64_t tag = ((uint64_t)a.epoch << 32) | phase;
-  if (threadIdx.x == 0) *flag = 1;
-  if (threadIdx.x == 0) st_dev64(mslot + blockIdx.x, tag);
+  if (threadIdx.x == 0) {
+    *flag = 1;
+    st_dev64(mslot + blockIdx.x, tag);
+  }
   __syncthreads();
-  if (blockIdx.x == g * kBarGroup) {
-    const int gsize = min(kBarGroup, G - g * kBarGroup);
-    if ((int)threadIdx.x < gsize && !wait_tag(a, mslot + g * kBarGroup + threadIdx.x, phase))
+  if (lu == gi * kBarGroup) {
+    const int gsize = min(kBarGroup, a.nch - gi * kBarGroup);
+    if ((int)threadIdx.x < gsize && !wait_tag(a, mslot + u0 + gi * kBarGroup + threadIdx.x, phase))
       *flag = 0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0 && *flag) st_dev64(gslot + 8 * g, tag);
+    if (threadIdx.x == 0 && *flag) st_dev64(gslot + 8 * gi, tag);
   }
-  if ((int)threadIdx.x < ngroups && !wait_tag(a, gslot + 8 * threadIdx.x, phase)) *flag = 0;
+  if ((int)threadIdx.x < ngs && !wait_tag(a, gslot + 8 * threadIdx.x, phase)) *flag = 0;
   __syncthreads();
   return *flag != 0;
 }
@@ -239,6 +259,132 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* scratch) {
   return total;
 }
 
+// Count, smallest high word and largest value of the nonzero values of a
+// thread (combined over the block by kth_reduce).
+struct KthStats {
+  uint32_t cnt = 0, hmin = 0xffffffffu;
+  uint64_t vmax = 0;
+  __device__ __forceinline__ void add(uint64_t v) {
+    if (v) {
+      ++cnt;
+      hmin = min(hmin, (uint32_t)(v >> 32));
+      vmax = max(vmax, v);
+    }
+  }
+};
+
+// Block-wide KthStats; red: 12 values of LDS.  Contains barriers.
+__device__ __forceinline__ KthStats kth_reduce(KthStats st, uint64_t* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  st.cnt = wave_sum_u32(st.cnt);
+  st.hmin = wave_min_u32(st.hmin);
+  st.vmax = wave_max_u64(st.vmax);
+  if (lane == 0) {
+    red[w] = st.cnt;
+    red[4 + w] = st.hmin;
+    red[8 + w] = st.vmax;
+  }
+  __syncthreads();
+  KthStats r;
+  r.cnt = 0;
+#pragma unroll
+  for (int x = 0; x < DT / 64; ++x) {
+    r.cnt += (uint32_t)red[x];
+    r.hmin = min(r.hmin, (uint32_t)red[4 + x]);
+    r.vmax = max(r.vmax, red[8 + x]);
+  }
+  __syncthreads();
+  return r;
+}
+
+// The kk-th largest of the nonzero values get(0), ..., get(n - 1), which must
+// be distinct, given their block-wide KthStats; 0 when fewer than kk of them
+// are nonzero.  Digits of (value - base), base = the smallest high word << 32,
+// are fixed from the top, 11 bits at a time, so that the first digit spreads
+// over the range the values actually take; once at most DT values share the
+// digits fixed so far they are gathered and the kk-th is found by ranking
+// them.  Every pass issues eight reads per thread before using them.
+// LDS: hist (2048 words), buf (DT values), red (12 values), scratch, res.
+template <class Get>
+__device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, const KthStats& st,
+                                                uint32_t* hist, uint64_t* buf, uint64_t* red,
+                                                uint32_t* scratch, uint32_t* res) {
+  auto each = [&](auto&& f) {
+    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * DT) {
+      uint64_t vv[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        // read at a clamped index unconditionally, then mask: the eight reads
+        // are issued back to back
+        const int i = i0 + x * DT;
+        const uint64_t v = get(min(i, n - 1));
+        vv[x] = i < n ? v : 0ull;
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) f(vv[x]);
+    }
+  };
+  if (kk == 0 || kk > st.cnt) return 0;
+  const uint64_t base = (uint64_t)st.hmin << 32;
+  const uint64_t span = st.vmax - base;
+  int hi = span ? 64 - __clzll((long long)span) : 0;   // low bits of (value - base) still open
+  uint64_t prefix = 0;                                   // (value - base) >> hi of the kk-th
+  uint32_t m = st.cnt;                                   // values sharing that prefix
+  auto matches = [&](uint64_t v) {
+    return v != 0 && (hi >= 64 || ((v - base) >> hi) == prefix);
+  };
+  while (m > (uint32_t)DT && hi > 0) {
+    const int bits = min(11, hi);
+    const int sh = hi - bits;
+    const int nbp = max(1 << bits, DT);
+    for (int i = threadIdx.x; i < nbp; i += DT) hist[i] = 0;
+    __syncthreads();
+    each([&](uint64_t v) {
+      if (matches(v)) atomicAdd(&hist[(uint32_t)((v - base) >> sh) & ((1u << bits) - 1u)], 1u);
+    });
+    __syncthreads();
+    pick_top(hist, nbp, kk, scratch, res);
+    const uint32_t d = res[0];
+    kk -= res[1];
+    m = hist[d];
+    prefix = (prefix << bits) | d;
+    hi = sh;
+    __syncthreads();
+  }
+  // gather: per-thread counts, a block scan for the slots, then the writes
+  uint32_t mine = 0;
+  each([&](uint64_t v) { mine += matches(v) ? 1u : 0u; });
+  uint32_t tot;
+  uint32_t sl = block_excl_scan<DT>(mine, scratch, tot);
+  each([&](uint64_t v) {
+    if (matches(v)) {
+      if (sl < (uint32_t)DT) buf[sl] = v;
+      ++sl;
+    }
+  });
+  __syncthreads();
+  const uint32_t mm = min(tot, (uint32_t)DT);
+  const uint32_t mm16 = (mm + 15u) & ~15u;
+  if (threadIdx.x >= mm && threadIdx.x < mm16) buf[threadIdx.x] = 0;   // below every value
+  __syncthreads();
+  if (threadIdx.x < mm) {
+    const uint64_t me = buf[threadIdx.x];
+    uint32_t r = 0;
+    for (uint32_t x = 0; x < mm16; x += 16) {
+      uint64_t o[16];
+#pragma unroll
+      for (int y = 0; y < 16; ++y) o[y] = buf[x + y];
+#pragma unroll
+      for (int y = 0; y < 16; ++y) r += o[y] > me;
+    }
+    if (r + 1 == kk) red[0] = me;
+  }
+  __syncthreads();
+  const uint64_t out = red[0];
+  __syncthreads();
+  return out;
+}
+
 __device__ __forceinline__ uint4 raw16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void widen(const uint4& u, float* o, const bf16_bits*) {
   o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
@@ -262,8 +408,9 @@ __device__ __forceinline__ void widen(const uint4& u, float* o, const float*) {
 // LDS use: [0, 16384) floats value tiles (4 x 16 KB, later the merge
 // buffer), then q (HCT x HD) and the per-wave (max, sum).
 template <typename TQ, int HD, int HCT>
-__device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
-                       int e0, int e1, const int* hsel, int nh, float* lds, bool q_ready) {
+__device__ __forceinline__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
+                       int e0, int e1, const int* hsel, int nh, float* lds, bool q_ready,
+                       const uint32_t* llist) {
   constexpr int EPV = 16 / (int)sizeof(TQ);   // elements per 16-byte load
   constexpr int LPR = HD / EPV;               // lanes per value row
   constexpr int KPI = 64 / LPR;               // value rows per load instruction
@@ -303,7 +450,7 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
     const int e = t0 + lane;
     int j = -1;
     if (e < e1) {
-      j = dense ? e : (int)ld_dev(lrow + e);
+      j = dense ? e : (int)(llist ? llist[e] : ld_dev(lrow + e));
       if (j < 0 || j > p) j = -1;
     }
     if constexpr (VLDS) {
@@ -455,8 +602,9 @@ __device__ void attend(const DecodeArgs& a, int row, int b, int n, int g, int s,
 // are merged through LDS; one partial (max, sum, acc) per head is written
 // for split s.
 template <int HD>
-__device__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
-                            int e0, int e1, const int* hsel, int nh, float* lds) {
+__device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, int s, bool dense,
+                            int e0, int e1, const int* hsel, int nh, float* lds,
+                            const uint32_t* llist) {
   constexpr int T = HD / 32;
   constexpr int NC = 16;                      // columns (heads) per item
   constexpr int LPR = HD / 8;                 // lanes per value row (16-byte pieces)
@@ -494,7 +642,7 @@ __device__ void attend_mfma(const DecodeArgs& a, int row, int b, int n, int g, i
     {
       const int e = t0 + lane;
       if (e < e1) {
-        jl = dense ? e : (int)ld_dev(lrow + e);
+        jl = dense ? e : (int)(llist ? llist[e] : ld_dev(lrow + e));
         if (jl < 0 || jl > p) jl = -1;
       }
     }
@@ -651,8 +799,8 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
   __shared__ int hsel[2][HCT];
   __shared__ int nsel[2];
   __shared__ uint32_t t0s[4], kk0s[4];
+  __shared__ uint64_t red[16];
 
-  const int G = gridDim.x;
   const int u = blockIdx.x;
   const bool has_unit = u < a.B * a.nch;
   const int b = has_unit ? u / a.nch : 0;
@@ -706,467 +854,601 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       }
     }
   }
+  if (!has_unit) return;   // a workgroup without a chunk has no further work
   // the sequence's per-row accumulators are cleared by its first unit
-  if (has_unit && !rows_ready(a, b, &flag)) return;
-  if (sp) {
-    __syncthreads();
-    for (int n = 0; n < N; ++n) {
-      const int vis = a.L - N + n + 1;
-      if (vis <= K) continue;
-      const int lim = min(clen, vis - j0);
-      for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
-      __syncthreads();
-      for (int jj = threadIdx.x; jj < lim; jj += DT)
-        atomicAdd(&hist[radix_key(lds[n * a.CH + jj]) >> 21], 1u);
-      __syncthreads();
-      uint32_t* gh = a.hist0 + ((size_t)b * N + n) * 2048;
-      for (int i = threadIdx.x; i < 2048; i += DT)
-        if (hist[i]) atomicAdd(&gh[i], hist[i]);
-      __syncthreads();
-    }
-  }
-  if (!grid_sync(a, 1u, &flag)) return;
+  if (!rows_ready(a, b, &flag)) return;
 
-  // ---------------------------------------------------------------- P2 candidates
-  // t0 = bin of the K-th key; keys above it are counted per chunk, keys in it
-  // become candidates and feed the second-digit histogram.
-  if (sp) {
-    for (int n = 0; n < N; ++n) {
-      const int vis = a.L - N + n + 1;
-      if (vis <= K) continue;
-      const int row = b * N + n;
-      const uint32_t* gh = a.hist0 + (size_t)row * 2048;
-#pragma unroll
-      for (int i = 0; i < 2048 / DT; ++i) hist[threadIdx.x + i * DT] = ld_dev(gh + threadIdx.x + i * DT);
+  // ------------------------------------------------ histogram selection phases
+  // H1: first-digit (top 11 key bits) histogram of every row -> global.
+  auto build_hist0 = [&]() {
+    if (sp) {
       __syncthreads();
-      pick_top(hist, 2048, (uint32_t)K, scratch, res);
-      const uint32_t t0 = res[0];
-      if (threadIdx.x == 0) {
-        t0s[n] = t0;
-        kk0s[n] = (uint32_t)K - res[1];
+      for (int n = 0; n < N; ++n) {
+        const int vis = a.L - N + n + 1;
+        if (vis <= K) continue;
+        const int lim = min(clen, vis - j0);
+        for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+        __syncthreads();
+        for (int jj = threadIdx.x; jj < lim; jj += DT)
+          atomicAdd(&hist[radix_key(lds[n * a.CH + jj]) >> 21], 1u);
+        __syncthreads();
+        uint32_t* gh = a.hist0 + ((size_t)b * N + n) * 2048;
+        for (int i = threadIdx.x; i < 2048; i += DT)
+          if (hist[i]) atomicAdd(&gh[i], hist[i]);
+        __syncthreads();
       }
-      const int lim = min(clen, vis - j0);
-      uint32_t above = 0, ncand = 0;
-      for (int jj = threadIdx.x; jj < lim; jj += DT) {
-        const uint32_t bin = radix_key(lds[n * a.CH + jj]) >> 21;
-        above += bin > t0;
-        ncand += bin == t0;
+    }
+  };
+  // H2: t0 = bin of the K-th key; keys above it are counted per chunk, keys in
+  // it become candidates and feed the second-digit histogram.
+  auto cand_phase = [&]() {
+    // t0 = bin of the K-th key; keys above it are counted per chunk, keys in it
+    // become candidates and feed the second-digit histogram.
+    if (sp) {
+      for (int n = 0; n < N; ++n) {
+        const int vis = a.L - N + n + 1;
+        if (vis <= K) continue;
+        const int row = b * N + n;
+        const uint32_t* gh = a.hist0 + (size_t)row * 2048;
+  #pragma unroll
+        for (int i = 0; i < 2048 / DT; ++i) hist[threadIdx.x + i * DT] = ld_dev(gh + threadIdx.x + i * DT);
+        __syncthreads();
+        pick_top(hist, 2048, (uint32_t)K, scratch, res);
+        const uint32_t t0 = res[0];
+        if (threadIdx.x == 0) {
+          t0s[n] = t0;
+          kk0s[n] = (uint32_t)K - res[1];
+        }
+        const int lim = min(clen, vis - j0);
+        uint32_t above = 0, ncand = 0;
+        for (int jj = threadIdx.x; jj < lim; jj += DT) {
+          const uint32_t bin = radix_key(lds[n * a.CH + jj]) >> 21;
+          above += bin > t0;
+          ncand += bin == t0;
+        }
+        uint32_t tot_c;
+        const uint32_t pre = block_excl_scan<DT>(ncand, scratch, tot_c);
+        const uint32_t tot_a = block_sum(above, scratch);
+        const int upg = (a.nch + kCandGroups - 1) / kCandGroups;   // chunks per group
+        const int grp = c / upg;
+        uint32_t base_slot = 0;
+        if (threadIdx.x == 0) {
+          // reserve this unit's slots in its group's region; the reply is
+          // needed only after the second-digit histogram below
+          if (tot_c) base_slot = atomicAdd(&a.cand_n[(size_t)row * kCandGroups + grp], tot_c);
+          st_dev(&a.cnt[(size_t)row * a.nch + c], tot_a);
+        }
+        for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+        __syncthreads();
+        for (int jj = threadIdx.x; jj < lim; jj += DT) {
+          const uint32_t key = radix_key(lds[n * a.CH + jj]);
+          if ((key >> 21) == t0) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
+        }
+        if (threadIdx.x == 0) res[2] = base_slot;
+        __syncthreads();
+        uint32_t slot = res[2] + pre;
+        uint64_t* cr = (uint64_t*)a.cand + (size_t)row * a.cand_cap + (size_t)grp * upg * a.CH;
+        for (int jj = threadIdx.x; jj < lim; jj += DT) {
+          const uint32_t key = radix_key(lds[n * a.CH + jj]);
+          if ((key >> 21) == t0) {
+            st_dev64(cr + slot, ((uint64_t)key << 32) | (uint32_t)(j0 + jj));
+            ++slot;
+          }
+        }
+        __syncthreads();
+        uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
+        for (int i = threadIdx.x; i < 2048; i += DT)
+          if (hist[i]) atomicAdd(&gh1[i], hist[i]);
+        __syncthreads();
       }
-      uint32_t tot_c;
-      const uint32_t pre = block_excl_scan<DT>(ncand, scratch, tot_c);
-      const uint32_t tot_a = block_sum(above, scratch);
-      const int upg = (a.nch + kCandGroups - 1) / kCandGroups;   // chunks per group
-      const int grp = c / upg;
-      uint32_t base_slot = 0;
-      if (threadIdx.x == 0) {
-        // reserve this unit's slots in its group's region; the reply is
-        // needed only after the second-digit histogram below
-        if (tot_c) base_slot = atomicAdd(&a.cand_n[(size_t)row * kCandGroups + grp], tot_c);
-        st_dev(&a.cnt[(size_t)row * a.nch + c], tot_a);
-      }
-      for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
-      __syncthreads();
-      for (int jj = threadIdx.x; jj < lim; jj += DT) {
-        const uint32_t key = radix_key(lds[n * a.CH + jj]);
-        if ((key >> 21) == t0) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
-      }
-      if (threadIdx.x == 0) res[2] = base_slot;
-      __syncthreads();
-      uint32_t slot = res[2] + pre;
-      uint64_t* cr = (uint64_t*)a.cand + (size_t)row * a.cand_cap + (size_t)grp * upg * a.CH;
-      for (int jj = threadIdx.x; jj < lim; jj += DT) {
-        const uint32_t key = radix_key(lds[n * a.CH + jj]);
-        if ((key >> 21) == t0) {
-          st_dev64(cr + slot, ((uint64_t)key << 32) | (uint32_t)(j0 + jj));
-          ++slot;
+    }
+  };
+  // H3 (ordered rows): every unit resolves its row's exact threshold itself:
+  // t1 from the second-digit histogram, then the few candidates sharing the
+  // top two digits give the exact K-th key T and the position cut P* for
+  // ties.  The unit's offset in the index row is the number of selected keys
+  // in the chunks before it.
+  auto select_phase = [&]() {
+    // Every unit resolves its row's exact threshold itself (no further
+    // barrier): t1 from the second-digit histogram, then the few candidates
+    // sharing the top two digits give the exact K-th key T and the position cut
+    // P* for ties.  The unit's offset in the index row is the number of
+    // selected keys in the chunks before it.
+    if (has_unit) {
+      for (int n = 0; n < N; ++n) {
+        const int row = b * N + n;
+        const int vis = a.L - N + n + 1;
+        uint32_t* lr = (uint32_t*)a.list + (size_t)row * K;
+        if (!sp) {
+          if (c == 0)
+            for (int i = threadIdx.x; i < K; i += DT) st_dev(lr + i, 0xffffffffu);
+          continue;
+        }
+        if (vis <= K) {
+          const int lim = min(clen, vis - j0);
+          for (int jj = threadIdx.x; jj < lim; jj += DT) st_dev(lr + j0 + jj, (uint32_t)(j0 + jj));
+          if (c == 0)
+            for (int i = vis + threadIdx.x; i < K; i += DT) st_dev(lr + i, 0xffffffffu);
+          continue;
+        }
+        const uint32_t t0 = t0s[n];
+        uint32_t kk = kk0s[n];
+        // one round trip: second-digit histogram, the groups' candidate counts
+        // and the keys above bin t0 in the chunks before this one
+        const uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
+        const uint32_t* cnt_row = a.cnt + (size_t)row * a.nch;
+        uint32_t* gpre = reinterpret_cast<uint32_t*>(lds + DSC);   // [kCandGroups + 1]
+        uint64_t* cl = reinterpret_cast<uint64_t*>(lds + DSC + 64);
+        const int cap_lds = (kLdsFloats - DSC - 64) / 2;
+        const int upg = (a.nch + kCandGroups - 1) / kCandGroups;
+        uint32_t before = 0;
+        {
+          uint32_t h8[2048 / DT];
+  #pragma unroll
+          for (int x = 0; x < 2048 / DT; ++x) h8[x] = ld_dev(gh1 + threadIdx.x + x * DT);
+          uint32_t gc = 0;
+          if (threadIdx.x < kCandGroups) gc = ld_dev(a.cand_n + (size_t)row * kCandGroups + threadIdx.x);
+          for (int u = threadIdx.x; u < c; u += DT) before += ld_dev(cnt_row + u);
+  #pragma unroll
+          for (int x = 0; x < 2048 / DT; ++x) hist[threadIdx.x + x * DT] = h8[x];
+          if (threadIdx.x < kCandGroups) gpre[threadIdx.x + 1] = gc;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          uint32_t acc = 0;
+          gpre[0] = 0;
+          for (int g2 = 1; g2 <= kCandGroups; ++g2) {
+            acc += gpre[g2];
+            gpre[g2] = acc;
+          }
+        }
+        __syncthreads();
+        const int nc = (int)gpre[kCandGroups];
+        pick_top(hist, 2048, kk, scratch, res);
+        const uint32_t t1 = res[0];
+        kk -= res[1];
+        const uint32_t m = hist[t1];              // candidates sharing digits t0, t1
+        const uint64_t* crg = (const uint64_t*)a.cand + (size_t)row * a.cand_cap;
+        // flat candidate index -> slot: the last group whose first index is <= f
+        // (a fixed-step search, so that several of them interleave)
+        auto grp_of = [&](uint32_t f) -> int {
+          int lo = 0;
+  #pragma unroll
+          for (int st = kCandGroups / 2; st > 0; st >>= 1)
+            if (gpre[lo + st] <= f) lo += st;
+          return lo;
+        };
+        auto cand_slot = [&](uint32_t f) -> size_t {
+          const int g2 = grp_of(f);
+          return (size_t)g2 * upg * a.CH + (f - gpre[g2]);
+        };
+        const uint32_t pfx = (t0 << 11) | t1;      // top 22 bits of T
+        const bool in_lds = m <= (uint32_t)cap_lds;
+        if (threadIdx.x == 0) res[3] = 0;
+        __syncthreads();
+        // one pass over the row's candidates: selected-for-sure ones before this
+        // chunk, and the ones sharing the top two digits (kept in LDS)
+        for (int i0 = 0; i0 < nc; i0 += DT * 8) {
+          size_t sl8[8];
+  #pragma unroll
+          for (int x = 0; x < 8; ++x) sl8[x] = cand_slot((uint32_t)(i0 + x * DT + threadIdx.x));
+          uint64_t v8[8];
+  #pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int f = i0 + x * DT + threadIdx.x;
+            v8[x] = (f < nc) ? ld_dev64(crg + sl8[x]) : 0ull;
+          }
+  #pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int f = i0 + x * DT + threadIdx.x;
+            if (f >= nc) continue;
+            const uint32_t key = (uint32_t)(v8[x] >> 32), pos = (uint32_t)v8[x];
+            const uint32_t top = key >> 10;
+            if (top > pfx && pos < (uint32_t)j0) ++before;
+            if (top == pfx && in_lds) cl[atomicAdd(&res[3], 1u)] = v8[x];
+          }
+        }
+        __syncthreads();
+        auto cand = [&](uint32_t i) -> uint64_t {
+          return in_lds ? cl[i] : ld_dev64(crg + cand_slot(i));
+        };
+        const uint32_t nl = in_lds ? m : (uint32_t)nc;   // entries to scan for the last digit
+        // T, the K-th key, and P*, the last position taken among keys equal to T
+        uint32_t T, pstar;
+        if (in_lds && m <= (uint32_t)DT) {
+          // few candidates share the top 22 bits: the kk-th of them under
+          // (key descending, position ascending) by counting the ones before it
+          if (threadIdx.x < m) {
+            const uint64_t me = cl[threadIdx.x];
+            const uint32_t key = (uint32_t)(me >> 32), pos = (uint32_t)me;
+            uint32_t r = 0;
+  #pragma unroll 8
+            for (uint32_t i = 0; i < m; ++i) {
+              const uint64_t o = cl[i];
+              const uint32_t ok = (uint32_t)(o >> 32), op = (uint32_t)o;
+              r += (ok > key) || (ok == key && op < pos);
+            }
+            if (r + 1 == kk) {
+              res[0] = key;
+              res[1] = pos;
+            }
+          }
+          __syncthreads();
+          T = res[0];
+          pstar = res[1];
+          __syncthreads();
+        } else {
+          // digit 3: key bits 9..0 among the candidates with prefix pfx
+          for (int i = threadIdx.x; i < 1024; i += DT) hist[i] = 0;
+          __syncthreads();
+          for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+            const uint32_t key = (uint32_t)(cand(i) >> 32);
+            if ((key >> 10) == pfx) atomicAdd(&hist[key & 1023u], 1u);
+          }
+          __syncthreads();
+          pick_top(hist, 1024, kk, scratch, res);
+          const uint32_t t2 = res[0];
+          kk -= res[1];
+          const uint32_t ties = hist[t2];
+          T = (pfx << 10) | t2;
+          __syncthreads();
+          pstar = 0x7fffffffu;
+          if (kk < ties) {
+            // kk-th smallest position among the keys equal to T
+            uint32_t pprefix = 0, pmask = 0;
+            const int pshift[3] = {20, 10, 0};
+            const int pbins[3] = {2048, 1024, 1024};
+            for (int lv = 0; lv < 3; ++lv) {
+              const int nb = pbins[lv], sh = pshift[lv];
+              for (int i = threadIdx.x; i < nb; i += DT) hist[i] = 0;
+              __syncthreads();
+              for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+                const uint64_t cd = cand(i);
+                const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
+                if (key == T && (pos & pmask) == pprefix) atomicAdd(&hist[(pos >> sh) & (nb - 1)], 1u);
+              }
+              __syncthreads();
+              pick_low(hist, nb, kk, scratch, res);
+              pprefix |= res[0] << sh;
+              pmask |= (uint32_t)(nb - 1) << sh;
+              kk -= res[1];
+              __syncthreads();
+            }
+            pstar = pprefix;
+          }
+        }
+        // selected candidates with the top-two-digit prefix before this chunk
+        for (uint32_t i = threadIdx.x; i < nl; i += DT) {
+          const uint64_t cd = cand(i);
+          const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
+          if ((key >> 10) == pfx && pos < (uint32_t)j0 && (key > T || (key == T && pos <= pstar)))
+            ++before;
+        }
+        uint32_t base = block_sum(before, scratch);
+        const int lim = min(clen, vis - j0);
+        // each thread takes 8 consecutive keys: one block scan per 8 * DT keys
+        for (int s0 = 0; s0 < lim; s0 += DT * 8) {
+          const int jb = s0 + threadIdx.x * 8;
+          uint32_t m8 = 0, c8 = 0;
+  #pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int jj = jb + x;
+            if (jj < lim) {
+              const uint32_t key = radix_key(lds[n * a.CH + jj]);
+              if (key > T || (key == T && (uint32_t)(j0 + jj) <= pstar)) {
+                m8 |= 1u << x;
+                ++c8;
+              }
+            }
+          }
+          uint32_t tot;
+          uint32_t o = base + block_excl_scan<DT>(c8, scratch, tot);
+  #pragma unroll
+          for (int x = 0; x < 8; ++x)
+            if ((m8 >> x) & 1u) {
+              if (o < (uint32_t)K) st_dev(lr + o, (uint32_t)(j0 + jb + x));
+              ++o;
+            }
+          base += tot;
         }
       }
-      __syncthreads();
-      uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
-      for (int i = threadIdx.x; i < 2048; i += DT)
-        if (hist[i]) atomicAdd(&gh1[i], hist[i]);
-      __syncthreads();
     }
-  }
-  if (!grid_sync(a, 2u, &flag)) return;
+  };
 
-  // q of this workgroup's first attention item: loaded now, moved to LDS once
-  // the selection below no longer needs that LDS
+  // ------------------------------------------------ attention items
+  // The last split of a (row, KV head, head chunk) to finish merges the
+  // partials and applies the gate (ticket counter), so no barrier follows.
+  // llist: the item row's index list in LDS, or null to read the global one.
   constexpr bool kMfma = sizeof(TQ) == 2;   // bf16 keys/values: MFMA attention
-  constexpr int NQ = kMfma ? 1 : (HCT * HD + DT - 1) / DT;
-  const int items = a.B * N * a.Hkv * a.S * a.nhc;
-  const bool q_pre = !kMfma && (int)blockIdx.x < items;
-  float qreg[NQ];
-  if (q_pre) {
-    const Item t = item_of(a, blockIdx.x);
-    const int rb = t.row / N, rn = t.row - rb * N;
+  const int per_s = ((K + a.S - 1) / a.S + 63) / 64 * 64;
+  const int per_d = ((a.L + a.S - 1) / a.S + 63) / 64 * 64;
+  auto run_item = [&](int it, const uint32_t* llist) {
+    const Item t = item_of(a, it);
+    const int row = t.row, g = t.g, s = t.s, hci = t.hci;
+    const int rb = row / N, rn = row - rb * N;
     item_heads<HCT>(a, t, rb, hsel, nsel);
     __syncthreads();
-    const int set = nsel[0] > 0 ? 0 : 1;
-    const int nh = nsel[set];
-#pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-      const int e = threadIdx.x + k * DT;
-      const int hh = e / HD, cq = e - hh * HD;
-      qreg[k] = (e < HCT * HD && hh < nh)
-                    ? ld_f((const TQ*)a.q, (((size_t)rb * N + rn) * a.Hq + hsel[set][hh]) * HD + cq) *
-                          a.scale_log2
-                    : 0.f;
+    const int ns = nsel[0], nd = nsel[1];
+    if (llist && g == 0 && hci == 0) {
+      // this split's part of the row's index list, from the LDS copy
+      const int e0 = s * per_s, e1 = min(K, e0 + per_s);
+      int32_t* lo = a.list + (size_t)row * K;
+      for (int e = e0 + (int)threadIdx.x; e < e1; e += DT) lo[e] = (int32_t)llist[e];
     }
-  }
+    const int vis = a.L - N + rn + 1;
+    if (ns > 0) {
+      const int e0 = s * per_s, e1 = min(K, e0 + per_s);
+      if constexpr (kMfma)
+        attend_mfma<HD>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds, llist);
+      else
+        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds, false, llist);
+    }
+    if (nd > 0) {
+      const int e0 = s * per_d, e1 = min(vis, e0 + per_d);
+      if constexpr (kMfma)
+        attend_mfma<HD>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds, nullptr);
+      else
+        attend<TQ, HD, HCT>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds, false, nullptr);
+    }
+    // ticket: the last split of this (row, g, hci) merges
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t tk = atomicAdd(&a.ticket[((size_t)row * a.Hkv + g) * a.nhc + hci], 1u);
+      res[0] = (tk + 1 == (uint32_t)a.S) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (res[0]) {
+      // One round of loads per 8 splits: this thread's accumulator elements
+      // (registers) and every (head, split) max and sum (to LDS), together
+      // with the gate and second-branch values; then each thread merges its
+      // (head, dim) elements over the splits with a running max.
+      constexpr int PS = HD + 4;                   // floats per partial
+      constexpr int NE = (HCT * HD + DT - 1) / DT;
+      constexpr int MB = 8;                        // splits per round
+      const int nh = ns + nd;
+      const int S = a.S;
+      float* mls = lds;                            // [nh][MB] (max, sum)
+      float Mx[NE], Lx[NE], Ax[NE], gv[NE], yv[NE];
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        Mx[k] = -INFINITY;
+        Lx[k] = 0.f;
+        Ax[k] = 0.f;
+        gv[k] = 1.f;
+        yv[k] = 0.f;
+      }
+      for (int s0 = 0; s0 < S; s0 += MB) {
+        const int sb = min(MB, S - s0);
+        float av[NE][MB];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+          const int e = threadIdx.x + k * DT;
+          const bool ok = e < nh * HD;
+          const int hh = e / HD, cth = e - hh * HD;
+          const int h = !ok ? 0 : (hh < ns ? hsel[0][hh] : hsel[1][hh - ns]);
+          const size_t orow = (size_t)row * a.Hq + h;
+          const float* pk = a.part + (orow * S + s0) * PS + 4 + cth;
+#pragma unroll
+          for (int x = 0; x < MB; ++x) av[k][x] = (ok && x < sb) ? ld_devf(pk + (size_t)x * PS) : 0.f;
+          if (s0 == 0 && ok && a.gate) {
+            gv[k] = a.gate[orow];
+            yv[k] = a.y2[orow * HD + cth];
+          }
+        }
+        // every slot of [nh][MB] is written (unused splits as max -inf,
+        // sum 0) so that the reads below need no predicate
+        for (int i2 = threadIdx.x; i2 < nh * MB; i2 += DT) {
+          const int hh = i2 / MB, sl = i2 - hh * MB;
+          float mval = -INFINITY, lval = 0.f;
+          if (sl < sb) {
+            const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
+            const float* ps = a.part + (((size_t)row * a.Hq + h) * S + s0 + sl) * PS;
+            mval = ld_devf(ps);
+            lval = ld_devf(ps + 1);
+          }
+          mls[2 * i2] = mval;
+          mls[2 * i2 + 1] = lval;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+          const int e = threadIdx.x + k * DT;
+          if (e >= nh * HD) continue;
+          const float* ml = mls + 2 * (e / HD) * MB;
+          float mv[MB], lv[MB];
+#pragma unroll
+          for (int x = 0; x < MB; ++x) {
+            mv[x] = ml[2 * x];
+            lv[x] = ml[2 * x + 1];
+          }
+          float mb = Mx[k];
+#pragma unroll
+          for (int x = 0; x < MB; ++x) mb = fmaxf(mb, mv[x]);
+          if (mb == -INFINITY) continue;
+          const float f0 = (Mx[k] == -INFINITY) ? 0.f : exp2f(Mx[k] - mb);
+          float l = Lx[k] * f0, acc = Ax[k] * f0;
+#pragma unroll
+          for (int x = 0; x < MB; ++x) {
+            const float f = exp2f(mv[x] - mb);   // 0 for an unused or empty split
+            l = fmaf(f, lv[x], l);
+            acc = fmaf(f, av[k][x], acc);
+          }
+          Mx[k] = mb;
+          Lx[k] = l;
+          Ax[k] = acc;
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const int e = threadIdx.x + k * DT;
+        if (e >= nh * HD) continue;
+        const int hh = e / HD, cth = e - hh * HD;
+        const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
+        const size_t orow = (size_t)row * a.Hq + h;
+        float val = (Lx[k] > 0.f) ? Ax[k] / Lx[k] : 0.f;
+        if (a.gate) val = fmaf(gv[k], val, (1.f - gv[k]) * yv[k]);
+        a.out[orow * HD + cth] = val;
+      }
+    }
+    __syncthreads();
+  };
 
-  // ---------------------------------------------------------------- P3 select + ordered rows
-  // Every unit resolves its row's exact threshold itself (no further
-  // barrier): t1 from the second-digit histogram, then the few candidates
-  // sharing the top two digits give the exact K-th key T and the position cut
-  // P* for ties.  The unit's offset in the index row is the number of
-  // selected keys in the chunks before it.
-  if (has_unit) {
-    for (int n = 0; n < N; ++n) {
-      const int row = b * N + n;
-      const int vis = a.L - N + n + 1;
-      uint32_t* lr = (uint32_t*)a.list + (size_t)row * K;
-      if (!sp) {
-        if (c == 0)
-          for (int i = threadIdx.x; i < K; i += DT) st_dev(lr + i, 0xffffffffu);
-        continue;
-      }
-      if (vis <= K) {
-        const int lim = min(clen, vis - j0);
-        for (int jj = threadIdx.x; jj < lim; jj += DT) st_dev(lr + j0 + jj, (uint32_t)(j0 + jj));
-        if (c == 0)
-          for (int i = vis + threadIdx.x; i < K; i += DT) st_dev(lr + i, 0xffffffffu);
-        continue;
-      }
-      const uint32_t t0 = t0s[n];
-      uint32_t kk = kk0s[n];
-      // one round trip: second-digit histogram, the groups' candidate counts
-      // and the keys above bin t0 in the chunks before this one
-      const uint32_t* gh1 = a.hist1 + (size_t)row * 2048;
-      const uint32_t* cnt_row = a.cnt + (size_t)row * a.nch;
-      uint32_t* gpre = reinterpret_cast<uint32_t*>(lds + DSC);   // [kCandGroups + 1]
-      uint64_t* cl = reinterpret_cast<uint64_t*>(lds + DSC + 64);
-      const int cap_lds = (kLdsFloats - DSC - 64) / 2;
-      const int upg = (a.nch + kCandGroups - 1) / kCandGroups;
-      uint32_t before = 0;
-      {
-        uint32_t h8[2048 / DT];
-#pragma unroll
-        for (int x = 0; x < 2048 / DT; ++x) h8[x] = ld_dev(gh1 + threadIdx.x + x * DT);
-        uint32_t gc = 0;
-        if (threadIdx.x < kCandGroups) gc = ld_dev(a.cand_n + (size_t)row * kCandGroups + threadIdx.x);
-        for (int u = threadIdx.x; u < c; u += DT) before += ld_dev(cnt_row + u);
-#pragma unroll
-        for (int x = 0; x < 2048 / DT; ++x) hist[threadIdx.x + x * DT] = h8[x];
-        if (threadIdx.x < kCandGroups) gpre[threadIdx.x + 1] = gc;
-      }
+  const int items_seq = N * a.Hkv * a.S * a.nhc;   // items of this sequence
+  uint32_t ph = 1;                                  // sequence barrier phase
+  const uint32_t* llist = nullptr;
+  bool slow = a.M == 0;
+  if (!slow) {
+    // ---------------------------------------------- candidate selection (N == 1)
+    // C1: the chunk's M largest keys under (key descending, position
+    // ascending), as order values key << 32 | ~position, go to the row's
+    // candidate array in position order, with the chunk's (M+1)-th value.
+    const int row = b;
+    const bool need = sp && a.L > K;
+    uint64_t* cbuf = reinterpret_cast<uint64_t*>(lds + a.CH);
+    auto ord_at = [&](int jj) -> uint64_t {
+      return ((uint64_t)radix_key(lds[jj]) << 32) | (uint32_t)~(uint32_t)(j0 + jj);
+    };
+    if (need) {
       __syncthreads();
-      if (threadIdx.x == 0) {
-        uint32_t acc = 0;
-        gpre[0] = 0;
-        for (int g2 = 1; g2 <= kCandGroups; ++g2) {
-          acc += gpre[g2];
-          gpre[g2] = acc;
+      uint64_t e = 0;
+      if (clen > a.M) {
+        KthStats st;
+        for (int i0 = threadIdx.x; i0 < clen; i0 += 8 * DT) {
+          uint64_t vv[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int i = i0 + x * DT;
+            const uint64_t v = ord_at(min(i, clen - 1));
+            vv[x] = i < clen ? v : 0ull;
+          }
+#pragma unroll
+          for (int x = 0; x < 8; ++x) st.add(vv[x]);
         }
+        e = kth_largest(clen, (uint32_t)a.M + 1, ord_at, kth_reduce(st, red), hist, cbuf, red,
+                        scratch, res);
       }
-      __syncthreads();
-      const int nc = (int)gpre[kCandGroups];
-      pick_top(hist, 2048, kk, scratch, res);
-      const uint32_t t1 = res[0];
-      kk -= res[1];
-      const uint32_t m = hist[t1];              // candidates sharing digits t0, t1
-      const uint64_t* crg = (const uint64_t*)a.cand + (size_t)row * a.cand_cap;
-      // flat candidate index -> slot: the last group whose first index is <= f
-      // (a fixed-step search, so that several of them interleave)
-      auto grp_of = [&](uint32_t f) -> int {
-        int lo = 0;
-#pragma unroll
-        for (int st = kCandGroups / 2; st > 0; st >>= 1)
-          if (gpre[lo + st] <= f) lo += st;
-        return lo;
-      };
-      auto cand_slot = [&](uint32_t f) -> size_t {
-        const int g2 = grp_of(f);
-        return (size_t)g2 * upg * a.CH + (f - gpre[g2]);
-      };
-      const uint32_t pfx = (t0 << 11) | t1;      // top 22 bits of T
-      const bool in_lds = m <= (uint32_t)cap_lds;
-      if (threadIdx.x == 0) res[3] = 0;
-      __syncthreads();
-      // one pass over the row's candidates: selected-for-sure ones before this
-      // chunk, and the ones sharing the top two digits (kept in LDS)
-      for (int i0 = 0; i0 < nc; i0 += DT * 8) {
-        size_t sl8[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) sl8[x] = cand_slot((uint32_t)(i0 + x * DT + threadIdx.x));
+      uint64_t* cw = a.fcand + (size_t)row * a.Cpad + (size_t)c * a.M;
+      uint32_t base = 0;
+      for (int s0 = 0; s0 < clen; s0 += DT * 8) {
+        const int jb = s0 + (int)threadIdx.x * 8;
         uint64_t v8[8];
+        uint32_t c8 = 0;
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
-          const int f = i0 + x * DT + threadIdx.x;
-          v8[x] = (f < nc) ? ld_dev64(crg + sl8[x]) : 0ull;
-        }
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int f = i0 + x * DT + threadIdx.x;
-          if (f >= nc) continue;
-          const uint32_t key = (uint32_t)(v8[x] >> 32), pos = (uint32_t)v8[x];
-          const uint32_t top = key >> 10;
-          if (top > pfx && pos < (uint32_t)j0) ++before;
-          if (top == pfx && in_lds) cl[atomicAdd(&res[3], 1u)] = v8[x];
-        }
-      }
-      __syncthreads();
-      auto cand = [&](uint32_t i) -> uint64_t {
-        return in_lds ? cl[i] : ld_dev64(crg + cand_slot(i));
-      };
-      const uint32_t nl = in_lds ? m : (uint32_t)nc;   // entries to scan for the last digit
-      // T, the K-th key, and P*, the last position taken among keys equal to T
-      uint32_t T, pstar;
-      if (in_lds && m <= (uint32_t)DT) {
-        // few candidates share the top 22 bits: the kk-th of them under
-        // (key descending, position ascending) by counting the ones before it
-        if (threadIdx.x < m) {
-          const uint64_t me = cl[threadIdx.x];
-          const uint32_t key = (uint32_t)(me >> 32), pos = (uint32_t)me;
-          uint32_t r = 0;
-#pragma unroll 8
-          for (uint32_t i = 0; i < m; ++i) {
-            const uint64_t o = cl[i];
-            const uint32_t ok = (uint32_t)(o >> 32), op = (uint32_t)o;
-            r += (ok > key) || (ok == key && op < pos);
-          }
-          if (r + 1 == kk) {
-            res[0] = key;
-            res[1] = pos;
-          }
-        }
-        __syncthreads();
-        T = res[0];
-        pstar = res[1];
-        __syncthreads();
-      } else {
-        // digit 3: key bits 9..0 among the candidates with prefix pfx
-        for (int i = threadIdx.x; i < 1024; i += DT) hist[i] = 0;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < nl; i += DT) {
-          const uint32_t key = (uint32_t)(cand(i) >> 32);
-          if ((key >> 10) == pfx) atomicAdd(&hist[key & 1023u], 1u);
-        }
-        __syncthreads();
-        pick_top(hist, 1024, kk, scratch, res);
-        const uint32_t t2 = res[0];
-        kk -= res[1];
-        const uint32_t ties = hist[t2];
-        T = (pfx << 10) | t2;
-        __syncthreads();
-        pstar = 0x7fffffffu;
-        if (kk < ties) {
-          // kk-th smallest position among the keys equal to T
-          uint32_t pprefix = 0, pmask = 0;
-          const int pshift[3] = {20, 10, 0};
-          const int pbins[3] = {2048, 1024, 1024};
-          for (int lv = 0; lv < 3; ++lv) {
-            const int nb = pbins[lv], sh = pshift[lv];
-            for (int i = threadIdx.x; i < nb; i += DT) hist[i] = 0;
-            __syncthreads();
-            for (uint32_t i = threadIdx.x; i < nl; i += DT) {
-              const uint64_t cd = cand(i);
-              const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
-              if (key == T && (pos & pmask) == pprefix) atomicAdd(&hist[(pos >> sh) & (nb - 1)], 1u);
-            }
-            __syncthreads();
-            pick_low(hist, nb, kk, scratch, res);
-            pprefix |= res[0] << sh;
-            pmask |= (uint32_t)(nb - 1) << sh;
-            kk -= res[1];
-            __syncthreads();
-          }
-          pstar = pprefix;
-        }
-      }
-      // selected candidates with the top-two-digit prefix before this chunk
-      for (uint32_t i = threadIdx.x; i < nl; i += DT) {
-        const uint64_t cd = cand(i);
-        const uint32_t key = (uint32_t)(cd >> 32), pos = (uint32_t)cd;
-        if ((key >> 10) == pfx && pos < (uint32_t)j0 && (key > T || (key == T && pos <= pstar)))
-          ++before;
-      }
-      uint32_t base = block_sum(before, scratch);
-      const int lim = min(clen, vis - j0);
-      // each thread takes 8 consecutive keys: one block scan per 8 * DT keys
-      for (int s0 = 0; s0 < lim; s0 += DT * 8) {
-        const int jb = s0 + threadIdx.x * 8;
-        uint32_t m8 = 0, c8 = 0;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int jj = jb + x;
-          if (jj < lim) {
-            const uint32_t key = radix_key(lds[n * a.CH + jj]);
-            if (key > T || (key == T && (uint32_t)(j0 + jj) <= pstar)) {
-              m8 |= 1u << x;
-              ++c8;
-            }
-          }
+          const uint64_t v = ord_at(min(jb + x, clen - 1));
+          v8[x] = jb + x < clen ? v : 0ull;
+          c8 += v8[x] > e;
         }
         uint32_t tot;
         uint32_t o = base + block_excl_scan<DT>(c8, scratch, tot);
 #pragma unroll
         for (int x = 0; x < 8; ++x)
-          if ((m8 >> x) & 1u) {
-            if (o < (uint32_t)K) st_dev(lr + o, (uint32_t)(j0 + jb + x));
+          if (v8[x] > e) {
+            if (o < (uint32_t)a.M) st_dev64(cw + o, v8[x]);
             ++o;
           }
         base += tot;
       }
+      for (int o = (int)base + (int)threadIdx.x; o < a.M; o += DT) st_dev64(cw + o, 0ull);
+      if (threadIdx.x == 0) st_dev64(a.fbound + (size_t)row * a.nch + c, e);
     }
-  }
-  if (q_pre) {
-    __syncthreads();
-    float* qs = lds + 16384;
+    if (!seq_sync(a, b, ph++, &flag)) return;
+    // C2: every unit with an attention item loads the row's candidates and
+    // finds their K-th largest value cK.  The candidates hold the row's top K
+    // when cK is above every chunk's (M+1)-th value (a key left out of a
+    // chunk is below that chunk's (M+1)-th, hence below cK, and K candidates
+    // are at or above cK); then the index list is the candidates at or above
+    // cK in position order, built in LDS.  Otherwise the sequence falls back
+    // to the histogram phases.
+    const int items_row = items_seq;
+    uint32_t* llw = hist;
+    if (!need) {
+      if (c >= items_row) return;
+      __syncthreads();
+      for (int e = threadIdx.x; e < K; e += DT) llw[e] = (sp && e < a.L) ? (uint32_t)e : 0xffffffffu;
+      __syncthreads();
+      llist = llw;
+    } else if (c < items_row) {
+      const int C = a.nch * a.M;
+      const uint64_t* cr = a.fcand + (size_t)row * a.Cpad;
+      KthStats st;
+      for (int i0 = 0; i0 < a.Cpad; i0 += DT * 16) {
+        uint64_t v16[16];
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-      const int e = threadIdx.x + k * DT;
-      if (e < HCT * HD) qs[e] = qreg[k];
-    }
-  }
-  if (!grid_sync(a, 3u, &flag)) return;
-
-  // ---------------------------------------------------------------- P4 attention + merge
-  // The last split of a (row, KV head, head chunk) to finish merges the
-  // partials and applies the gate (ticket counter), so no further grid
-  // barrier is needed.
-  {
-    const int per_s = ((K + a.S - 1) / a.S + 63) / 64 * 64;
-    const int per_d = ((a.L + a.S - 1) / a.S + 63) / 64 * 64;
-    for (int it = blockIdx.x; it < items; it += G) {
-      const Item t = item_of(a, it);
-      const int row = t.row, g = t.g, s = t.s, hci = t.hci;
-      const int rb = row / N, rn = row - rb * N;
-      item_heads<HCT>(a, t, rb, hsel, nsel);
-      __syncthreads();
-      const int ns = nsel[0], nd = nsel[1];
-      const int vis = a.L - N + rn + 1;
-      const bool first = it == (int)blockIdx.x;   // q already in LDS
-      if (ns > 0) {
-        const int e0 = s * per_s, e1 = min(K, e0 + per_s);
-        if constexpr (kMfma)
-          attend_mfma<HD>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds);
-        else
-          attend<TQ, HD, HCT>(a, row, rb, rn, g, s, false, e0, e1, hsel[0], ns, lds, first);
+        for (int x = 0; x < 16; ++x) {
+          const int i = i0 + x * DT + (int)threadIdx.x;
+          const uint64_t v = ld_dev64(cr + min(i, C - 1));
+          v16[x] = i < C ? v : 0ull;
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int i = i0 + x * DT + (int)threadIdx.x;
+          if (i < a.Cpad) cbuf[i] = v16[x];
+          st.add(v16[x]);
+        }
       }
-      if (nd > 0) {
-        const int e0 = s * per_d, e1 = min(vis, e0 + per_d);
-        if constexpr (kMfma)
-          attend_mfma<HD>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds);
-        else
-          attend<TQ, HD, HCT>(a, row, rb, rn, g, s, true, e0, e1, hsel[1], nd, lds,
-                              first && ns == 0);
+      uint64_t emax = 0;
+      for (int i = threadIdx.x; i < a.nch; i += DT)
+        emax = max(emax, ld_dev64(a.fbound + (size_t)row * a.nch + i));
+      emax = wave_max_u64(emax);
+      if ((threadIdx.x & 63) == 0) red[12 + (threadIdx.x >> 6)] = emax;
+      const KthStats all = kth_reduce(st, red);
+      emax = max(max(red[12], red[13]), max(red[14], red[15]));
+      const uint64_t ck = kth_largest(a.Cpad, (uint32_t)K, [&](int i) { return cbuf[i]; }, all,
+                                      hist, cbuf + a.Cpad, red, scratch, res);
+      const bool valid = ck != 0 && ck > emax;
+      if (c == 0 && threadIdx.x == 0)
+        st_dev64(a.verdict + 8 * b, ((uint64_t)a.epoch << 32) | (valid ? 1u : 2u));
+      if (valid) {
+        // thread t takes entries [t * per, (t + 1) * per), per <= 32 and even
+        const int per = a.Cpad / DT;
+        const uint64_t* mine = cbuf + (size_t)threadIdx.x * per;
+        uint32_t sel = 0;
+#pragma unroll
+        for (int x = 0; x < 32; x += 2) {
+          const ulonglong2 v2 = *reinterpret_cast<const ulonglong2*>(mine + min(x, per - 2));
+          const bool in = x < per;
+          sel |= (in && v2.x >= ck ? 1u : 0u) << x;
+          sel |= (in && v2.y >= ck ? 1u : 0u) << (x + 1);
+        }
+        uint32_t tot;
+        uint32_t o = block_excl_scan<DT>((uint32_t)__popc(sel), scratch, tot);
+        while (sel) {
+          const int x = __ffs(sel) - 1;
+          sel &= sel - 1;
+          llw[o++] = ~(uint32_t)mine[x];
+        }
+        __syncthreads();
+        llist = llw;
+      } else {
+        slow = true;
       }
-      // ticket: the last split of this (row, g, hci) merges
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    } else {
+      // no attention item here: this unit is needed again only if the
+      // sequence falls back (unit 0 publishes the verdict)
       if (threadIdx.x == 0) {
-        const uint32_t tk = atomicAdd(&a.ticket[((size_t)row * a.Hkv + g) * a.nhc + hci], 1u);
-        res[0] = (tk + 1 == (uint32_t)a.S) ? 1u : 0u;
+        res[0] = 0;
+        if (wait_tag(a, a.verdict + 8 * b, 1u)) res[0] = (uint32_t)ld_dev64(a.verdict + 8 * b);
       }
       __syncthreads();
-      if (res[0]) {
-        // One round of loads per 8 splits: this thread's accumulator elements
-        // (registers) and every (head, split) max and sum (to LDS), together
-        // with the gate and second-branch values; then each thread merges its
-        // (head, dim) elements over the splits with a running max.
-        constexpr int PS = HD + 4;                   // floats per partial
-        constexpr int NE = (HCT * HD + DT - 1) / DT;
-        constexpr int MB = 8;                        // splits per round
-        const int nh = ns + nd;
-        const int S = a.S;
-        float* mls = lds;                            // [nh][MB] (max, sum)
-        float Mx[NE], Lx[NE], Ax[NE], gv[NE], yv[NE];
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-          Mx[k] = -INFINITY;
-          Lx[k] = 0.f;
-          Ax[k] = 0.f;
-          gv[k] = 1.f;
-          yv[k] = 0.f;
-        }
-        for (int s0 = 0; s0 < S; s0 += MB) {
-          const int sb = min(MB, S - s0);
-          float av[NE][MB];
-#pragma unroll
-          for (int k = 0; k < NE; ++k) {
-            const int e = threadIdx.x + k * DT;
-            const bool ok = e < nh * HD;
-            const int hh = e / HD, cth = e - hh * HD;
-            const int h = !ok ? 0 : (hh < ns ? hsel[0][hh] : hsel[1][hh - ns]);
-            const size_t orow = (size_t)row * a.Hq + h;
-            const float* pk = a.part + (orow * S + s0) * PS + 4 + cth;
-#pragma unroll
-            for (int x = 0; x < MB; ++x) av[k][x] = (ok && x < sb) ? ld_devf(pk + (size_t)x * PS) : 0.f;
-            if (s0 == 0 && ok && a.gate) {
-              gv[k] = a.gate[orow];
-              yv[k] = a.y2[orow * HD + cth];
-            }
-          }
-          // every slot of [nh][MB] is written (unused splits as max -inf,
-          // sum 0) so that the reads below need no predicate
-          for (int i2 = threadIdx.x; i2 < nh * MB; i2 += DT) {
-            const int hh = i2 / MB, sl = i2 - hh * MB;
-            float mval = -INFINITY, lval = 0.f;
-            if (sl < sb) {
-              const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
-              const float* ps = a.part + (((size_t)row * a.Hq + h) * S + s0 + sl) * PS;
-              mval = ld_devf(ps);
-              lval = ld_devf(ps + 1);
-            }
-            mls[2 * i2] = mval;
-            mls[2 * i2 + 1] = lval;
-          }
-          __syncthreads();
-#pragma unroll
-          for (int k = 0; k < NE; ++k) {
-            const int e = threadIdx.x + k * DT;
-            if (e >= nh * HD) continue;
-            const float* ml = mls + 2 * (e / HD) * MB;
-            float mv[MB], lv[MB];
-#pragma unroll
-            for (int x = 0; x < MB; ++x) {
-              mv[x] = ml[2 * x];
-              lv[x] = ml[2 * x + 1];
-            }
-            float mb = Mx[k];
-#pragma unroll
-            for (int x = 0; x < MB; ++x) mb = fmaxf(mb, mv[x]);
-            if (mb == -INFINITY) continue;
-            const float f0 = (Mx[k] == -INFINITY) ? 0.f : exp2f(Mx[k] - mb);
-            float l = Lx[k] * f0, acc = Ax[k] * f0;
-#pragma unroll
-            for (int x = 0; x < MB; ++x) {
-              const float f = exp2f(mv[x] - mb);   // 0 for an unused or empty split
-              l = fmaf(f, lv[x], l);
-              acc = fmaf(f, av[k][x], acc);
-            }
-            Mx[k] = mb;
-            Lx[k] = l;
-            Ax[k] = acc;
-          }
-          __syncthreads();
-        }
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-          const int e = threadIdx.x + k * DT;
-          if (e >= nh * HD) continue;
-          const int hh = e / HD, cth = e - hh * HD;
-          const int h = hh < ns ? hsel[0][hh] : hsel[1][hh - ns];
-          const size_t orow = (size_t)row * a.Hq + h;
-          float val = (Lx[k] > 0.f) ? Ax[k] / Lx[k] : 0.f;
-          if (a.gate) val = fmaf(gv[k], val, (1.f - gv[k]) * yv[k]);
-          a.out[orow * HD + cth] = val;
-        }
-      }
+      const uint32_t vd = res[0];
       __syncthreads();
+      if (vd != 2u) return;
+      slow = true;
     }
   }
+  if (slow) {
+    build_hist0();
+    if (!seq_sync(a, b, ph++, &flag)) return;
+    cand_phase();
+    if (!seq_sync(a, b, ph++, &flag)) return;
+    select_phase();
+    if (!seq_sync(a, b, ph++, &flag)) return;
+    llist = nullptr;
+  }
+  for (int il = c; il < items_seq; il += a.nch) run_item(b * items_seq + il, llist);
 }
 
 template <typename TI, int DIDX, typename TQ, int HD>
@@ -1245,6 +1527,24 @@ bool decode_plan(const Dims& D, int grid, DecodePlan& P) {
   // workgroup busy with one 64-key pass each
   P.S = std::max(1, (D.K + 255) / 256);
   P.cand_cap = kCandGroups * ((nch + kCandGroups - 1) / kCandGroups) * (int)ch;
+  // One-exchange selection for single-row sequences: each chunk passes on
+  // its M largest keys, about twice its expected share of the top K plus a
+  // margin, as many as the LDS holds next to the chunk's scores.
+  P.M = 0;
+  P.Cpad = 0;
+  if (D.N == 1 && D.K <= 2048) {
+    const int avail = (kLdsFloats - (int)ch - 2 * DT) / 2;   // 8-byte slots left in LDS
+    const int share = (D.K + nch - 1) / nch;
+    int M = (int)std::min<long long>(ch, 2LL * share + 16);
+    // padded to whole blocks of 4 * DT slots: the list pass reads an even
+    // count of at most 32 per thread
+    auto padded = [&](int m) { return ((long long)nch * m + 4 * DT - 1) / (4 * DT) * (4 * DT); };
+    while (M > 0 && (padded(M) > avail || padded(M) > 32 * DT)) --M;
+    if (M > 0 && (long long)M * nch >= D.K && (M == ch || 2 * M >= 3 * share)) {
+      P.M = M;
+      P.Cpad = (int)padded(M);
+    }
+  }
   return true;
 }
 
@@ -1256,6 +1556,7 @@ size_t decode_ws_bound(const Dims& D) {
   P.S = (D.K + 63) / 64;
   P.nhc = D.Hq;
   P.cand_cap = D.L + kCandGroups * DSC;   // groups * (chunks per group) * CH < L + groups * CH
+  P.Cpad = D.N == 1 ? (kLdsFloats - 256 - 2 * DT) / 2 : 0;
   return decode_ws_bytes(D, P);
 }
 
@@ -1263,7 +1564,8 @@ size_t decode_ws_bound(const Dims& D) {
 // words, both digit histograms, candidate counts, tickets), then per-chunk
 // counts, candidates and attention partials.
 struct DecodeLayout {
-  size_t ctl, rowtag, hist0, hist1, cand_n, ticket, cnt, cand, part, total;
+  size_t ctl, rowtag, sgslot, verdict, hist0, hist1, cand_n, ticket, cnt, cand, fcand, fbound,
+      part, total;
 };
 
 DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
@@ -1273,12 +1575,16 @@ DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
   size_t off = 0;
   Lo.ctl = off;    off = al(off + ctl_words64(kMaxGrid) * 8);
   Lo.rowtag = off; off = al(off + rows * 8);
+  Lo.sgslot = off; off = al(off + (size_t)D.B * ((P.nch + kBarGroup - 1) / kBarGroup) * 64);
+  Lo.verdict = off; off = al(off + (size_t)D.B * 64);
   Lo.hist0 = off;  off = al(off + rows * 2048 * 4);
   Lo.hist1 = off;  off = al(off + rows * 2048 * 4);
   Lo.cand_n = off; off = al(off + rows * kCandGroups * 4);
   Lo.ticket = off; off = al(off + rows * D.Hkv * (size_t)P.nhc * 4);
   Lo.cnt = off;    off = al(off + rows * (size_t)P.nch * 4);
   Lo.cand = off;   off = al(off + rows * (size_t)P.cand_cap * 8);
+  Lo.fcand = off;  off = al(off + rows * (size_t)P.Cpad * 8);
+  Lo.fbound = off; off = al(off + (P.Cpad ? rows * (size_t)P.nch * 8 : 0));
   Lo.part = off;   off = al(off + rows * D.Hq * (size_t)P.S * (D.d + 4) * 4);
   Lo.total = off;
   return Lo;
@@ -1330,6 +1636,11 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   a.cnt = (uint32_t*)(w + Lo.cnt);
   a.cand = (uint64_t*)(w + Lo.cand);
   a.part = (float*)(w + Lo.part);
+  a.fcand = (uint64_t*)(w + Lo.fcand);
+  a.fbound = (uint64_t*)(w + Lo.fbound);
+  a.sgslot = (uint64_t*)(w + Lo.sgslot);
+  a.verdict = (uint64_t*)(w + Lo.verdict);
+  a.M = P.M; a.Cpad = P.Cpad;
   a.B = D.B; a.N = D.N; a.L = D.L; a.Hq = D.Hq; a.Hkv = D.Hkv; a.K = D.K;
   a.CH = P.CH; a.nch = P.nch; a.S = P.S; a.nhc = P.nhc; a.cand_cap = P.cand_cap;
   a.scale_log2 = D.scale * kLog2e;

@@ -74,7 +74,9 @@ struct DecodePlan {
   int nch = 0;       // chunks per sequence
   int S = 1;         // attention key splits
   int nhc = 1;       // head chunks per KV head
-  int cand_cap = 0;  // candidate slots per row
+  int cand_cap = 0;  // candidate slots per row (histogram selection)
+  int M = 0;         // candidates per chunk for the one-exchange selection (0: not used)
+  int Cpad = 0;      // candidate slots per row for it (nch * M, padded)
 };
 // Co-resident grid for the decode kernel of these dims on the current device
 // (0 if it cannot be determined, e.g. without a GPU).
