@@ -43,6 +43,7 @@
 #include <unistd.h>
 
 #include <chrono>
+#include <cmath>
 #include <map>
 #include <mutex>
 
@@ -131,7 +132,7 @@ __device__ __forceinline__ void raise_error(const DecodeArgs& a) {
 }
 
 // Bounded wait of one thread for a tagged word; false on timeout or error.
-__device__ bool wait_tag(const DecodeArgs& a, const uint64_t* p, uint32_t at_least) {
+__device__ __forceinline__ bool wait_tag(const DecodeArgs& a, const uint64_t* p, uint32_t at_least) {
   uint32_t spins = 0;
   while (!tagged(ld_dev64(p), a.epoch, at_least)) {
     if (tagged(ld_dev64(a.ctl), a.epoch, 1u)) return false;
@@ -152,7 +153,7 @@ __device__ bool wait_tag(const DecodeArgs& a, const uint64_t* p, uint32_t at_lea
 // every unit waits for the sequence's group slots.  Each thread first waits
 // for its own outstanding memory operations, so the stores before the
 // barrier have completed when the slot is written.
-__device__ bool seq_sync(const DecodeArgs& a, int b, uint32_t phase, int* flag) {
+__device__ __forceinline__ bool seq_sync(const DecodeArgs& a, int b, uint32_t phase, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int u0 = b * a.nch;
@@ -183,7 +184,7 @@ __device__ bool seq_sync(const DecodeArgs& a, int b, uint32_t phase, int* flag) 
 // Row accumulators (both histograms, candidate count, merge tickets) are
 // cleared at the start of every launch by the first unit of the sequence;
 // the row's tag then reads "ready" for this launch.
-__device__ void clear_rows(const DecodeArgs& a, int b) {
+__device__ __forceinline__ void clear_rows(const DecodeArgs& a, int b) {
   const int nt = a.Hkv * a.nhc;
   for (int n = 0; n < a.N; ++n) {
     const int row = b * a.N + n;
@@ -203,7 +204,7 @@ __device__ void clear_rows(const DecodeArgs& a, int b) {
 }
 
 // Waits until the rows of sequence b are cleared for this launch.
-__device__ bool rows_ready(const DecodeArgs& a, int b, int* flag) {
+__device__ __forceinline__ bool rows_ready(const DecodeArgs& a, int b, int* flag) {
   __syncthreads();
   if (threadIdx.x == 0) *flag = 1;
   __syncthreads();
@@ -213,7 +214,7 @@ __device__ bool rows_ready(const DecodeArgs& a, int b, int* flag) {
 }
 
 // kk-th largest (from the top) over hist[0..nb): bin and count above it.
-__device__ void pick_top(const uint32_t* hist, int nb, uint32_t kk, uint32_t* scratch,
+__device__ __forceinline__ void pick_top(const uint32_t* hist, int nb, uint32_t kk, uint32_t* scratch,
                          uint32_t* res) {
   const int per = nb / DT;
   const int base = threadIdx.x * per;
@@ -234,7 +235,7 @@ __device__ void pick_top(const uint32_t* hist, int nb, uint32_t kk, uint32_t* sc
 }
 
 // kk-th smallest (from the bottom) over hist[0..nb): bin and count below it.
-__device__ void pick_low(const uint32_t* hist, int nb, uint32_t kk, uint32_t* scratch,
+__device__ __forceinline__ void pick_low(const uint32_t* hist, int nb, uint32_t kk, uint32_t* scratch,
                          uint32_t* res) {
   const int per = nb / DT;
   const int base = threadIdx.x * per;
@@ -297,80 +298,153 @@ __device__ __forceinline__ KthStats kth_reduce(KthStats st, uint64_t* red) {
   return r;
 }
 
-// The kk-th largest of the nonzero values get(0), ..., get(n - 1), which must
-// be distinct, given their block-wide KthStats; 0 when fewer than kk of them
-// are nonzero.  Digits of (value - base), base = the smallest high word << 32,
-// are fixed from the top, 11 bits at a time, so that the first digit spreads
-// over the range the values actually take; once at most DT values share the
-// digits fixed so far they are gathered and the kk-th is found by ranking
-// them.  Every pass issues eight reads per thread before using them.
-// LDS: hist (2048 words), buf (DT values), red (12 values), scratch, res.
+// The kk-th largest (1 <= kk <= m) of the order values get(0), ..., get(n - 1)
+// (key << 32 | ~position, distinct; 0 marks an empty slot, so a value is
+// present iff its low word is nonzero).  m values are present, their keys
+// are at least hmin and (value - (hmin << 32)) < 2^hi.  Digits of
+// (value - (hmin << 32)) are fixed from the top, 11 bits at a time, with
+// 32-bit arithmetic while they lie in the key word; once at most DT values
+// share the digits fixed so far they are gathered and the kk-th is found by
+// ranking them.  Each level costs two barriers: wave 0 alone turns the
+// histogram into the digit (32 bins per lane, one DPP scan) and clears the
+// bins it read.
+// Caller: hist[0 .. 2048), buf[0 .. DT) and res[2] must be zero, and visible
+// to every thread (written before a barrier).  On return hist is zero again;
+// buf and res[2] are not.
+// LDS: hist (2048 words), buf (DT values), red (1 value), res (4 words).
 template <class Get>
-__device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, const KthStats& st,
-                                                uint32_t* hist, uint64_t* buf, uint64_t* red,
-                                                uint32_t* scratch, uint32_t* res) {
-  auto each = [&](auto&& f) {
-    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * DT) {
-      uint64_t vv[8];
+__device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, uint32_t hmin, int hi,
+                                                uint32_t m, uint32_t* hist, uint64_t* buf,
+                                                uint64_t* red, uint32_t* res) {
+  const int iters = (n + 8 * DT - 1) / (8 * DT);   // the same for every thread
+  auto load8 = [&](int k, uint64_t* vv) {
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        // read at a clamped index unconditionally, then mask: the eight reads
-        // are issued back to back
-        const int i = i0 + x * DT;
-        const uint64_t v = get(min(i, n - 1));
-        vv[x] = i < n ? v : 0ull;
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) f(vv[x]);
+    for (int x = 0; x < 8; ++x) {
+      // read at a clamped index unconditionally, then mask
+      const int i = (int)threadIdx.x + k * 8 * DT + x * DT;
+      const uint64_t v = get(min(i, n - 1));
+      vv[x] = i < n ? v : 0ull;
     }
+    // keep the reads together: without this the scheduler puts each read
+    // next to its use and waits for it
+    __builtin_amdgcn_sched_barrier(0);
   };
-  if (kk == 0 || kk > st.cnt) return 0;
-  const uint64_t base = (uint64_t)st.hmin << 32;
-  const uint64_t span = st.vmax - base;
-  int hi = span ? 64 - __clzll((long long)span) : 0;   // low bits of (value - base) still open
-  uint64_t prefix = 0;                                   // (value - base) >> hi of the kk-th
-  uint32_t m = st.cnt;                                   // values sharing that prefix
-  auto matches = [&](uint64_t v) {
-    return v != 0 && (hi >= 64 || ((v - base) >> hi) == prefix);
+  const int lane = threadIdx.x & 63;
+  uint64_t prefix = 0;   // (value - (hmin << 32)) >> hi of the kk-th
+  auto matches = [&](uint64_t v) -> bool {
+    const uint32_t lo = (uint32_t)v, kd = (uint32_t)(v >> 32) - hmin;
+    if (lo == 0) return false;
+    if (hi >= 64) return true;
+    if (hi >= 32) return (kd >> (hi - 32)) == (uint32_t)prefix;
+    return ((((uint64_t)kd << 32) | lo) >> hi) == prefix;
   };
   while (m > (uint32_t)DT && hi > 0) {
     const int bits = min(11, hi);
     const int sh = hi - bits;
-    const int nbp = max(1 << bits, DT);
-    for (int i = threadIdx.x; i < nbp; i += DT) hist[i] = 0;
+    const uint32_t nbm = (1u << bits) - 1u;
+    for (int k = 0; k < iters; ++k) {
+      uint64_t vv[8];
+      load8(k, vv);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const uint64_t v = vv[x];
+        if (matches(v)) {
+          const uint32_t kd = (uint32_t)(v >> 32) - hmin;
+          const uint32_t dg = sh >= 32 ? (kd >> (sh - 32)) & nbm
+                                       : (uint32_t)(((((uint64_t)kd) << 32) | (uint32_t)v) >> sh) & nbm;
+          atomicAdd(&hist[dg], 1u);
+        }
+      }
+    }
     __syncthreads();
-    each([&](uint64_t v) {
-      if (matches(v)) atomicAdd(&hist[(uint32_t)((v - base) >> sh) & ((1u << bits) - 1u)], 1u);
-    });
+    if (threadIdx.x < 64) {
+      // lane l holds bins [top_l - per, top_l), lane 0 the highest
+      const int nb = 1 << bits;
+      const int per = max(1, nb >> 6);
+      const int top = nb - per * lane;
+      uint32_t hv[32];
+      if (per == 32) {
+        uint4* hp = reinterpret_cast<uint4*>(hist + top - 32);
+        uint4 u8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u8[q] = hp[q];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint4 u4 = u8[q];
+          hv[31 - 4 * q] = u4.x;
+          hv[30 - 4 * q] = u4.y;
+          hv[29 - 4 * q] = u4.z;
+          hv[28 - 4 * q] = u4.w;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) hp[q] = make_uint4(0, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int bin = top - 1 - j;
+          hv[j] = (j < per && bin >= 0) ? hist[bin] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int bin = top - 1 - j;
+          if (j < per && bin >= 0) hist[bin] = 0;
+        }
+      }
+      uint32_t sum = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) sum += hv[j];
+      const uint32_t incl = wave_incl_scan(sum);          // values in bins >= this lane's lowest
+      const uint64_t hit = __ballot(incl >= kk);
+      const int L = __ffsll((long long)hit) - 1;
+      if (lane == L) {
+        uint32_t above = incl - sum;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          if (j < per && above < kk && above + hv[j] >= kk) {
+            res[0] = (uint32_t)(top - 1 - j);
+            res[1] = above;
+            res[3] = hv[j];
+          }
+          above += hv[j];
+        }
+      }
+    }
     __syncthreads();
-    pick_top(hist, nbp, kk, scratch, res);
     const uint32_t d = res[0];
     kk -= res[1];
-    m = hist[d];
+    m = res[3];
     prefix = (prefix << bits) | d;
     hi = sh;
-    __syncthreads();
   }
-  // gather: per-thread counts, a block scan for the slots, then the writes
-  uint32_t mine = 0;
-  each([&](uint64_t v) { mine += matches(v) ? 1u : 0u; });
-  uint32_t tot;
-  uint32_t sl = block_excl_scan<DT>(mine, scratch, tot);
-  each([&](uint64_t v) {
-    if (matches(v)) {
-      if (sl < (uint32_t)DT) buf[sl] = v;
-      ++sl;
+  // gather: one LDS atomic per wave and group of eight values for the slots
+  for (int k = 0; k < iters; ++k) {
+    uint64_t vv[8];
+    load8(k, vv);
+    uint32_t msk = 0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) msk |= (matches(vv[x]) ? 1u : 0u) << x;
+    const uint32_t c8 = (uint32_t)__popc(msk);
+    const uint32_t incl = wave_incl_scan(c8);
+    const uint32_t wt = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (wt) {
+      uint32_t wb = 0;
+      if (lane == 63) wb = atomicAdd(&res[2], wt);
+      uint32_t sl = (uint32_t)__builtin_amdgcn_readlane((int)wb, 63) + incl - c8;
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        if ((msk >> x) & 1u) {
+          if (sl < (uint32_t)DT) buf[sl] = vv[x];
+          ++sl;
+        }
     }
-  });
+  }
   __syncthreads();
-  const uint32_t mm = min(tot, (uint32_t)DT);
-  const uint32_t mm16 = (mm + 15u) & ~15u;
-  if (threadIdx.x >= mm && threadIdx.x < mm16) buf[threadIdx.x] = 0;   // below every value
-  __syncthreads();
+  const uint32_t mm = min(res[2], (uint32_t)DT);
   if (threadIdx.x < mm) {
     const uint64_t me = buf[threadIdx.x];
     uint32_t r = 0;
-    for (uint32_t x = 0; x < mm16; x += 16) {
+    for (uint32_t x = 0; x < mm; x += 16) {   // buf beyond mm is zero, below every value
       uint64_t o[16];
 #pragma unroll
       for (int y = 0; y < 16; ++y) o[y] = buf[x + y];
@@ -380,9 +454,7 @@ __device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, con
     if (r + 1 == kk) red[0] = me;
   }
   __syncthreads();
-  const uint64_t out = red[0];
-  __syncthreads();
-  return out;
+  return red[0];
 }
 
 __device__ __forceinline__ uint4 raw16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -855,6 +927,12 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
     }
   }
   if (!has_unit) return;   // a workgroup without a chunk has no further work
+  if (a.M) {
+    // state the candidate selection expects (published by the barriers below)
+    for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+    reinterpret_cast<uint64_t*>(lds + a.CH)[threadIdx.x] = 0;
+    if (threadIdx.x == 0) res[2] = 0;
+  }
   // the sequence's per-row accumulators are cleared by its first unit
   if (!rows_ready(a, b, &flag)) return;
 
@@ -1313,22 +1391,8 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
     if (need) {
       __syncthreads();
       uint64_t e = 0;
-      if (clen > a.M) {
-        KthStats st;
-        for (int i0 = threadIdx.x; i0 < clen; i0 += 8 * DT) {
-          uint64_t vv[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int i = i0 + x * DT;
-            const uint64_t v = ord_at(min(i, clen - 1));
-            vv[x] = i < clen ? v : 0ull;
-          }
-#pragma unroll
-          for (int x = 0; x < 8; ++x) st.add(vv[x]);
-        }
-        e = kth_largest(clen, (uint32_t)a.M + 1, ord_at, kth_reduce(st, red), hist, cbuf, red,
-                        scratch, res);
-      }
+      if (clen > a.M)
+        e = kth_largest(clen, (uint32_t)a.M + 1, ord_at, 0u, 64, (uint32_t)clen, hist, cbuf, red, res);
       uint64_t* cw = a.fcand + (size_t)row * a.Cpad + (size_t)c * a.M;
       uint32_t base = 0;
       for (int s0 = 0; s0 < clen; s0 += DT * 8) {
@@ -1339,8 +1403,10 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
         for (int x = 0; x < 8; ++x) {
           const uint64_t v = ord_at(min(jb + x, clen - 1));
           v8[x] = jb + x < clen ? v : 0ull;
-          c8 += v8[x] > e;
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) c8 += v8[x] > e;
         uint32_t tot;
         uint32_t o = base + block_excl_scan<DT>(c8, scratch, tot);
 #pragma unroll
@@ -1382,6 +1448,7 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
           const uint64_t v = ld_dev64(cr + min(i, C - 1));
           v16[x] = i < C ? v : 0ull;
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int i = i0 + x * DT + (int)threadIdx.x;
@@ -1394,10 +1461,18 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
         emax = max(emax, ld_dev64(a.fbound + (size_t)row * a.nch + i));
       emax = wave_max_u64(emax);
       if ((threadIdx.x & 63) == 0) red[12 + (threadIdx.x >> 6)] = emax;
+      cbuf[a.Cpad + threadIdx.x] = 0;   // the selection's gather buffer
+      if (threadIdx.x == 0) res[2] = 0;
       const KthStats all = kth_reduce(st, red);
       emax = max(max(red[12], red[13]), max(red[14], red[15]));
-      const uint64_t ck = kth_largest(a.Cpad, (uint32_t)K, [&](int i) { return cbuf[i]; }, all,
-                                      hist, cbuf + a.Cpad, red, scratch, res);
+      // first digit over the range the candidates take
+      const uint64_t span = all.vmax - ((uint64_t)all.hmin << 32);
+      const int chi = span ? 64 - __clzll((long long)span) : 0;
+      const uint64_t ck =
+          all.cnt >= (uint32_t)K
+              ? kth_largest(a.Cpad, (uint32_t)K, [&](int i) { return cbuf[i]; }, all.hmin, chi, all.cnt,
+                            hist, cbuf + a.Cpad, red, res)
+              : 0ull;
       const bool valid = ck != 0 && ck > emax;
       if (c == 0 && threadIdx.x == 0)
         st_dev64(a.verdict + 8 * b, ((uint64_t)a.epoch << 32) | (valid ? 1u : 2u));
@@ -1406,12 +1481,16 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
         const int per = a.Cpad / DT;
         const uint64_t* mine = cbuf + (size_t)threadIdx.x * per;
         uint32_t sel = 0;
+        ulonglong2 v2[16];
+#pragma unroll
+        for (int x = 0; x < 32; x += 2)
+          v2[x / 2] = *reinterpret_cast<const ulonglong2*>(mine + min(x, per - 2));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < 32; x += 2) {
-          const ulonglong2 v2 = *reinterpret_cast<const ulonglong2*>(mine + min(x, per - 2));
           const bool in = x < per;
-          sel |= (in && v2.x >= ck ? 1u : 0u) << x;
-          sel |= (in && v2.y >= ck ? 1u : 0u) << (x + 1);
+          sel |= (in && v2[x / 2].x >= ck ? 1u : 0u) << x;
+          sel |= (in && v2[x / 2].y >= ck ? 1u : 0u) << (x + 1);
         }
         uint32_t tot;
         uint32_t o = block_excl_scan<DT>((uint32_t)__popc(sel), scratch, tot);
@@ -1528,14 +1607,16 @@ bool decode_plan(const Dims& D, int grid, DecodePlan& P) {
   P.S = std::max(1, (D.K + 255) / 256);
   P.cand_cap = kCandGroups * ((nch + kCandGroups - 1) / kCandGroups) * (int)ch;
   // One-exchange selection for single-row sequences: each chunk passes on
-  // its M largest keys, about twice its expected share of the top K plus a
-  // margin, as many as the LDS holds next to the chunk's scores.
+  // its M largest keys.  A chunk's count of top-K keys is close to binomial
+  // with mean `share` for keys in no particular order, so share plus four
+  // standard deviations plus 8 is exceeded with probability below 1e-6 per
+  // chunk; capped by what the LDS holds next to the chunk's scores.
   P.M = 0;
   P.Cpad = 0;
   if (D.N == 1 && D.K <= 2048) {
     const int avail = (kLdsFloats - (int)ch - 2 * DT) / 2;   // 8-byte slots left in LDS
     const int share = (D.K + nch - 1) / nch;
-    int M = (int)std::min<long long>(ch, 2LL * share + 16);
+    int M = (int)std::min<long long>(ch, share + (int)std::ceil(4.0 * std::sqrt((double)share)) + 8);
     // padded to whole blocks of 4 * DT slots: the list pass reads an even
     // count of at most 32 per thread
     auto padded = [&](int m) { return ((long long)nch * m + 4 * DT - 1) / (4 * DT) * (4 * DT); };
