@@ -78,6 +78,10 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   const uint32_t r = wave_incl_dpp(x, 0xffffffffu, [](uint32_t p, uint32_t q) { return min(p, q); });
   return (uint32_t)__builtin_amdgcn_readlane((int)r, 63);
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  const uint32_t r = wave_incl_dpp(x, 0u, [](uint32_t p, uint32_t q) { return max(p, q); });
+  return (uint32_t)__builtin_amdgcn_readlane((int)r, 63);
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #define DSA_DPP_MAX64(ctrl, rmask)                                                              \
   {                                                                                             \

@@ -17,7 +17,9 @@
 // Single-row sequences (N == 1), when the LDS holds every chunk's candidates:
 //   C1  each chunk passes on its M largest keys under (key descending,
 //       position ascending), as order values key << 32 | ~position in
-//       position order, and its (M+1)-th value.
+//       position order; atomics keep the row's largest (M+1)-th value and
+//       the key range of its candidates.  The first digit of the chunk's
+//       selection is counted during P1.
 //   C2  after one barrier, every unit with an attention item loads the row's
 //       candidates, finds their K-th largest value cK and checks that cK is
 //       above every chunk's (M+1)-th value; if so the index list is the
@@ -76,11 +78,13 @@ struct DecodeArgs {
   uint64_t* cand;    // [rows][cand_cap] key << 32 | position, one region per group
   float* part;       // [rows][Hq][S][HD+4]: max, sum, 2 pad, accumulator
   uint64_t* fcand;   // [rows][Cpad] each chunk's M largest order values, in position order
-  uint64_t* fbound;  // [rows][nch] each chunk's (M+1)-th largest order value (0: none)
   uint64_t* sgslot;  // [B][ngroups][8] epoch-tagged group slots of the sequence barriers
   uint64_t* verdict; // [B][8] epoch-tagged: 1 = candidates hold the top K, 2 = they may not
   int B, N, L, Hq, Hkv, K, CH, nch, S, nhc, cand_cap;
+  uint64_t* fstat;   // [rows][nch][4 waves][2]: (largest | smallest << 32) candidate key of
+                     // the wave's share of the chunk, and the chunk's (M+1)-th value
   int M, Cpad;       // candidates per chunk (0: histogram selection only), padded row size
+  int ccnt;          // candidates present per row
   float scale_log2;
   uint32_t epoch;    // distinct per launch; tags every control word
 };
@@ -196,6 +200,7 @@ __device__ __forceinline__ void clear_rows(const DecodeArgs& a, int b) {
     }
     for (int i = threadIdx.x; i < nt; i += DT) st_dev(a.ticket + (size_t)row * nt + i, 0u);
     if (threadIdx.x < kCandGroups) st_dev(a.cand_n + (size_t)row * kCandGroups + threadIdx.x, 0u);
+
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -260,44 +265,6 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* scratch) {
   return total;
 }
 
-// Count, smallest high word and largest value of the nonzero values of a
-// thread (combined over the block by kth_reduce).
-struct KthStats {
-  uint32_t cnt = 0, hmin = 0xffffffffu;
-  uint64_t vmax = 0;
-  __device__ __forceinline__ void add(uint64_t v) {
-    if (v) {
-      ++cnt;
-      hmin = min(hmin, (uint32_t)(v >> 32));
-      vmax = max(vmax, v);
-    }
-  }
-};
-
-// Block-wide KthStats; red: 12 values of LDS.  Contains barriers.
-__device__ __forceinline__ KthStats kth_reduce(KthStats st, uint64_t* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  st.cnt = wave_sum_u32(st.cnt);
-  st.hmin = wave_min_u32(st.hmin);
-  st.vmax = wave_max_u64(st.vmax);
-  if (lane == 0) {
-    red[w] = st.cnt;
-    red[4 + w] = st.hmin;
-    red[8 + w] = st.vmax;
-  }
-  __syncthreads();
-  KthStats r;
-  r.cnt = 0;
-#pragma unroll
-  for (int x = 0; x < DT / 64; ++x) {
-    r.cnt += (uint32_t)red[x];
-    r.hmin = min(r.hmin, (uint32_t)red[4 + x]);
-    r.vmax = max(r.vmax, red[8 + x]);
-  }
-  __syncthreads();
-  return r;
-}
-
 // The kk-th largest (1 <= kk <= m) of the order values get(0), ..., get(n - 1)
 // (key << 32 | ~position, distinct; 0 marks an empty slot, so a value is
 // present iff its low word is nonzero).  m values are present, their keys
@@ -308,14 +275,15 @@ __device__ __forceinline__ KthStats kth_reduce(KthStats st, uint64_t* red) {
 // ranking them.  Each level costs two barriers: wave 0 alone turns the
 // histogram into the digit (32 bins per lane, one DPP scan) and clears the
 // bins it read.
-// Caller: hist[0 .. 2048), buf[0 .. DT) and res[2] must be zero, and visible
-// to every thread (written before a barrier).  On return hist is zero again;
-// buf and res[2] are not.
+// Caller: buf[0 .. DT) and res[2] must be zero and hist[0 .. 2048) either zero
+// or, with hist_ready, the counts of the first digit, all visible to every
+// thread (written before a barrier).  On return hist is zero again; buf and
+// res[2] are not.
 // LDS: hist (2048 words), buf (DT values), red (1 value), res (4 words).
 template <class Get>
 __device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, uint32_t hmin, int hi,
-                                                uint32_t m, uint32_t* hist, uint64_t* buf,
-                                                uint64_t* red, uint32_t* res) {
+                                                uint32_t m, bool hist_ready, uint32_t* hist,
+                                                uint64_t* buf, uint64_t* red, uint32_t* res) {
   const int iters = (n + 8 * DT - 1) / (8 * DT);   // the same for every thread
   auto load8 = [&](int k, uint64_t* vv) {
 #pragma unroll
@@ -342,7 +310,7 @@ __device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, uin
     const int bits = min(11, hi);
     const int sh = hi - bits;
     const uint32_t nbm = (1u << bits) - 1u;
-    for (int k = 0; k < iters; ++k) {
+    for (int k = 0; k < (hist_ready ? 0 : iters); ++k) {
       uint64_t vv[8];
       load8(k, vv);
 #pragma unroll
@@ -416,6 +384,11 @@ __device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, uin
     m = res[3];
     prefix = (prefix << bits) | d;
     hi = sh;
+    hist_ready = false;
+  }
+  if (hist_ready) {
+    // counts handed in but no level needed: leave the histogram cleared
+    for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
   }
   // gather: one LDS atomic per wave and group of eight values for the slots
   for (int k = 0; k < iters; ++k) {
@@ -883,6 +856,8 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
   const int N = a.N, K = a.K;
 
   if (has_unit && c == 0) clear_rows(a, b);
+  // single-row sequence on the candidate selection
+  const bool cand_sel = a.M > 0 && sp && a.L > K;
 
   // ---------------------------------------------------------------- P1 scan
   if (sp) {
@@ -1381,9 +1356,10 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
     // ---------------------------------------------- candidate selection (N == 1)
     // C1: the chunk's M largest keys under (key descending, position
     // ascending), as order values key << 32 | ~position, go to the row's
-    // candidate array in position order, with the chunk's (M+1)-th value.
+    // candidate array in position order, with the key range of each wave's
+    // share and the chunk's (M+1)-th value.
     const int row = b;
-    const bool need = sp && a.L > K;
+    const bool need = cand_sel;
     uint64_t* cbuf = reinterpret_cast<uint64_t*>(lds + a.CH);
     auto ord_at = [&](int jj) -> uint64_t {
       return ((uint64_t)radix_key(lds[jj]) << 32) | (uint32_t)~(uint32_t)(j0 + jj);
@@ -1392,9 +1368,11 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       __syncthreads();
       uint64_t e = 0;
       if (clen > a.M)
-        e = kth_largest(clen, (uint32_t)a.M + 1, ord_at, 0u, 64, (uint32_t)clen, hist, cbuf, red, res);
+        e = kth_largest(clen, (uint32_t)a.M + 1, ord_at, 0u, 64, (uint32_t)clen, false, hist, cbuf,
+                        red, res);
       uint64_t* cw = a.fcand + (size_t)row * a.Cpad + (size_t)c * a.M;
       uint32_t base = 0;
+      uint32_t kmx = 0, kmn = 0xffffffffu;
       for (int s0 = 0; s0 < clen; s0 += DT * 8) {
         const int jb = s0 + (int)threadIdx.x * 8;
         uint64_t v8[8];
@@ -1414,20 +1392,30 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
           if (v8[x] > e) {
             if (o < (uint32_t)a.M) st_dev64(cw + o, v8[x]);
             ++o;
+            kmx = max(kmx, (uint32_t)(v8[x] >> 32));
+            kmn = min(kmn, (uint32_t)(v8[x] >> 32));
           }
         base += tot;
       }
+      // this wave's candidate key range and the chunk's (M+1)-th value
+      kmx = wave_max_u32(kmx);
+      kmn = wave_min_u32(kmn);
+      if ((threadIdx.x & 63) == 0) {
+        uint64_t* fs = a.fstat + (((size_t)row * a.nch + c) * 4 + (threadIdx.x >> 6)) * 2;
+        st_dev64(fs, (uint64_t)kmx | ((uint64_t)kmn << 32));
+        st_dev64(fs + 1, e);
+      }
       for (int o = (int)base + (int)threadIdx.x; o < a.M; o += DT) st_dev64(cw + o, 0ull);
-      if (threadIdx.x == 0) st_dev64(a.fbound + (size_t)row * a.nch + c, e);
     }
     if (!seq_sync(a, b, ph++, &flag)) return;
-    // C2: every unit with an attention item loads the row's candidates and
-    // finds their K-th largest value cK.  The candidates hold the row's top K
-    // when cK is above every chunk's (M+1)-th value (a key left out of a
-    // chunk is below that chunk's (M+1)-th, hence below cK, and K candidates
-    // are at or above cK); then the index list is the candidates at or above
-    // cK in position order, built in LDS.  Otherwise the sequence falls back
-    // to the histogram phases.
+    // C2: every unit with an attention item loads the row's candidates,
+    // counting their first digit as they arrive, and finds their K-th
+    // largest value cK.  The candidates hold the row's top K when cK is above
+    // every chunk's (M+1)-th value (a key left out of a chunk is below that
+    // chunk's (M+1)-th, hence below cK, and K candidates are at or above cK);
+    // then the index list is the candidates at or above cK in position
+    // order, built in LDS.  Otherwise the sequence falls back to the
+    // histogram phases.
     const int items_row = items_seq;
     uint32_t* llw = hist;
     if (!need) {
@@ -1439,9 +1427,21 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
     } else if (c < items_row) {
       const int C = a.nch * a.M;
       const uint64_t* cr = a.fcand + (size_t)row * a.Cpad;
-      KthStats st;
-      for (int i0 = 0; i0 < a.Cpad; i0 += DT * 16) {
-        uint64_t v16[16];
+      // the row's candidate key range and largest left-out value, from the
+      // per-wave records of C1 (loaded together with the candidates)
+      const int nst = a.nch * 4;
+      const uint64_t* fs = a.fstat + (size_t)row * nst * 2;
+      uint32_t kmax = 0, kmin = 0xffffffffu;
+      uint64_t emax = 0;
+      uint64_t sw[8][2];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = min((int)threadIdx.x + q * DT, nst - 1);
+        sw[q][0] = ld_dev64(fs + 2 * i);
+        sw[q][1] = ld_dev64(fs + 2 * i + 1);
+      }
+      uint64_t v16[16];
+      auto load16 = [&](int i0) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int i = i0 + x * DT + (int)threadIdx.x;
@@ -1449,30 +1449,54 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
           v16[x] = i < C ? v : 0ull;
         }
         __builtin_amdgcn_sched_barrier(0);
+      };
+      load16(0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if ((int)threadIdx.x + q * DT < nst) {
+          kmax = max(kmax, (uint32_t)sw[q][0]);
+          kmin = min(kmin, (uint32_t)(sw[q][0] >> 32));
+          emax = max(emax, sw[q][1]);
+        }
+      kmax = wave_max_u32(kmax);
+      kmin = wave_min_u32(kmin);
+      emax = wave_max_u64(emax);
+      if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6] = kmax;
+        red[4 + (threadIdx.x >> 6)] = kmin;
+        red[8 + (threadIdx.x >> 6)] = emax;
+      }
+      cbuf[a.Cpad + threadIdx.x] = 0;   // the selection's gather buffer
+      if (threadIdx.x == 0) res[2] = 0;
+      __syncthreads();
+      kmax = (uint32_t)max(max(red[0], red[1]), max(red[2], red[3]));
+      kmin = (uint32_t)min(min(red[4], red[5]), min(red[6], red[7]));
+      emax = max(max(red[8], red[9]), max(red[10], red[11]));
+      // first digit over the key range the candidates take, counted as the
+      // candidates are stored
+      const int chi = kmax > kmin ? 64 - __clz(kmax - kmin) : 32;
+      const int bits = min(11, chi);
+      const int sh = chi - bits;
+      const uint32_t nbm = (1u << bits) - 1u;
+      for (int i0 = 0; i0 < a.Cpad; i0 += DT * 16) {
+        if (i0) load16(i0);
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int i = i0 + x * DT + (int)threadIdx.x;
-          if (i < a.Cpad) cbuf[i] = v16[x];
-          st.add(v16[x]);
+          const uint64_t v = v16[x];
+          if (i < a.Cpad) cbuf[i] = v;
+          if ((uint32_t)v != 0u) {
+            const uint32_t kd = (uint32_t)(v >> 32) - kmin;
+            const uint32_t dg = sh >= 32 ? (kd >> (sh - 32)) & nbm
+                                         : (uint32_t)(((((uint64_t)kd) << 32) | (uint32_t)v) >> sh) & nbm;
+            atomicAdd(&hist[dg], 1u);
+          }
         }
       }
-      uint64_t emax = 0;
-      for (int i = threadIdx.x; i < a.nch; i += DT)
-        emax = max(emax, ld_dev64(a.fbound + (size_t)row * a.nch + i));
-      emax = wave_max_u64(emax);
-      if ((threadIdx.x & 63) == 0) red[12 + (threadIdx.x >> 6)] = emax;
-      cbuf[a.Cpad + threadIdx.x] = 0;   // the selection's gather buffer
-      if (threadIdx.x == 0) res[2] = 0;
-      const KthStats all = kth_reduce(st, red);
-      emax = max(max(red[12], red[13]), max(red[14], red[15]));
-      // first digit over the range the candidates take
-      const uint64_t span = all.vmax - ((uint64_t)all.hmin << 32);
-      const int chi = span ? 64 - __clzll((long long)span) : 0;
       const uint64_t ck =
-          all.cnt >= (uint32_t)K
-              ? kth_largest(a.Cpad, (uint32_t)K, [&](int i) { return cbuf[i]; }, all.hmin, chi, all.cnt,
-                            hist, cbuf + a.Cpad, red, res)
-              : 0ull;
+          a.ccnt >= K ? kth_largest(a.Cpad, (uint32_t)K, [&](int i) { return cbuf[i]; }, kmin, chi,
+                                    (uint32_t)a.ccnt, true, hist, cbuf + a.Cpad, red, res)
+                      : 0ull;
       const bool valid = ck != 0 && ck > emax;
       if (c == 0 && threadIdx.x == 0)
         st_dev64(a.verdict + 8 * b, ((uint64_t)a.epoch << 32) | (valid ? 1u : 2u));
@@ -1613,7 +1637,8 @@ bool decode_plan(const Dims& D, int grid, DecodePlan& P) {
   // chunk; capped by what the LDS holds next to the chunk's scores.
   P.M = 0;
   P.Cpad = 0;
-  if (D.N == 1 && D.K <= 2048) {
+  // (the per-wave records of a row, 4 per chunk, are read 8 per thread)
+  if (D.N == 1 && D.K <= 2048 && nch * 4 <= 8 * DT) {
     const int avail = (kLdsFloats - (int)ch - 2 * DT) / 2;   // 8-byte slots left in LDS
     const int share = (D.K + nch - 1) / nch;
     int M = (int)std::min<long long>(ch, share + (int)std::ceil(4.0 * std::sqrt((double)share)) + 8);
@@ -1645,7 +1670,7 @@ size_t decode_ws_bound(const Dims& D) {
 // words, both digit histograms, candidate counts, tickets), then per-chunk
 // counts, candidates and attention partials.
 struct DecodeLayout {
-  size_t ctl, rowtag, sgslot, verdict, hist0, hist1, cand_n, ticket, cnt, cand, fcand, fbound,
+  size_t ctl, rowtag, sgslot, verdict, hist0, hist1, cand_n, ticket, cnt, cand, fcand, fstat,
       part, total;
 };
 
@@ -1665,7 +1690,7 @@ DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
   Lo.cnt = off;    off = al(off + rows * (size_t)P.nch * 4);
   Lo.cand = off;   off = al(off + rows * (size_t)P.cand_cap * 8);
   Lo.fcand = off;  off = al(off + rows * (size_t)P.Cpad * 8);
-  Lo.fbound = off; off = al(off + (P.Cpad ? rows * (size_t)P.nch * 8 : 0));
+  Lo.fstat = off;  off = al(off + (P.Cpad ? rows * (size_t)P.nch * 64 : 0));
   Lo.part = off;   off = al(off + rows * D.Hq * (size_t)P.S * (D.d + 4) * 4);
   Lo.total = off;
   return Lo;
@@ -1718,10 +1743,11 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   a.cand = (uint64_t*)(w + Lo.cand);
   a.part = (float*)(w + Lo.part);
   a.fcand = (uint64_t*)(w + Lo.fcand);
-  a.fbound = (uint64_t*)(w + Lo.fbound);
   a.sgslot = (uint64_t*)(w + Lo.sgslot);
   a.verdict = (uint64_t*)(w + Lo.verdict);
   a.M = P.M; a.Cpad = P.Cpad;
+  a.ccnt = P.M ? (P.nch - 1) * P.M + std::min(D.L - (P.nch - 1) * P.CH, P.M) : 0;
+  a.fstat = (uint64_t*)(w + Lo.fstat);
   a.B = D.B; a.N = D.N; a.L = D.L; a.Hq = D.Hq; a.Hkv = D.Hkv; a.K = D.K;
   a.CH = P.CH; a.nch = P.nch; a.S = P.S; a.nhc = P.nhc; a.cand_cap = P.cand_cap;
   a.scale_log2 = D.scale * kLog2e;
