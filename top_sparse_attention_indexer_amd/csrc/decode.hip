@@ -99,7 +99,7 @@ __device__ __forceinline__ bool seq_sparse(const uint8_t* route, int b, int Hq) 
 // Cross-workgroup data is written with device-scope atomic stores and read
 // with device-scope atomic loads: both bypass the per-XCD L2 copies, so no
 // L2 writeback / invalidate (the expensive part of a device-scope fence) is
-// needed around the grid barrier.  Counters and histograms use atomic RMWs.
+// needed around the sequence barriers.  Counters and histograms use atomic RMWs.
 __device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
