@@ -173,11 +173,12 @@ def test_edge_shapes(name, w, use_gate, announce):
     check_rows(w, x, out, idx, rows=rows, use_gate=use_gate)
 
 
-def test_long_context_prefill_chunk(announce):
-    """A 256-row prefill chunk at the end of a 300000-token context (query rows
-    over a long cache through the bottom-right causal alignment): rows wider
-    than 65536 keys take the multi-pass top-k."""
-    w = _w(1, 256, 300000, 8, 2, 128, 64, 2048, seed=21)
+@pytest.mark.parametrize("N,L", [(256, 300000), (64, 1048576)])
+def test_long_context_prefill_chunk(N, L, announce):
+    """A prefill chunk at the end of a long context (query rows over a long
+    cache through the bottom-right causal alignment), up to a 1 M-token
+    cache: rows wider than 65536 keys take the multi-pass top-k."""
+    w = _w(1, N, L, 8, 2, 128, 64, 2048, seed=21)
     x = synth.make_inputs(w)
     announce(f"fused_forward {w}")
     out, idx = run_fused(w, x)
