@@ -160,6 +160,11 @@ EDGE = [
     # single-row decode with fewer visible keys than K, and a short last chunk
     ("decode_L_lt_K", _w(2, 1, 300, 4, 2, 64, 32, 512)),
     ("decode_ragged_chunk", _w(5, 1, 3333, 8, 2, 128, 64, 700, seed=12)),
+    # single-row decode: fp32 K/V (VALU attention reading the LDS index list),
+    # K = 1, and a context that is one chunk
+    ("decode_fp32_single_row", _w(3, 1, 9000, 4, 2, 64, 32, 333, dt="fp32")),
+    ("decode_K_1", _w(3, 1, 5000, 4, 1, 64, 32, 1)),
+    ("decode_one_chunk", _w(2, 1, 200, 4, 2, 64, 32, 100)),
 ]
 
 
