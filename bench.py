@@ -117,7 +117,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode in this build).", file=sys.stderr)
+              "(the library runs on one GPU; it has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
 
     import torch
