@@ -47,6 +47,16 @@
  * re-entrant across threads and streams if their workspaces are distinct.
  * Preconditions the library cannot check: finite inputs (NaN/Inf give
  * undefined selections); device pointers of the stated sizes.
+ *
+ * Co-residency.  dsa_fused_forward with at most 4 query rows per sequence
+ * (decode) runs as one launch whose workgroups exchange data while they run,
+ * so all of them must be resident on the device at once; the grid is sized
+ * from the occupancy query to fill the whole device, and the library orders
+ * its own such launches across streams.  Other work running on the device at
+ * the same time (another stream of the caller, another process) can keep
+ * some workgroups from starting.  Every wait between workgroups is bounded:
+ * a wait that gives up makes the outputs of its sequence NaN and its index
+ * rows -1, and dsa_exec_status() then returns DSA_ERR_EXEC.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -63,7 +73,8 @@ typedef enum {
   DSA_ERR_INVALID_ARG = 1, /* null required pointer, bad size, misalignment   */
   DSA_ERR_UNSUPPORTED = 2, /* head_dim / idx_dim / dtype outside the built set */
   DSA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than needed    */
-  DSA_ERR_HIP = 4          /* a launch failed (hipGetLastError)                */
+  DSA_ERR_HIP = 4,         /* a launch failed (hipGetLastError)                */
+  DSA_ERR_EXEC = 5         /* a launch ran but gave up (see dsa_exec_status)   */
 } dsa_status;
 
 typedef enum { DSA_FP32 = 0, DSA_BF16 = 1 } dsa_dtype;
@@ -128,6 +139,21 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx,
                              const uint8_t* route, float* out,
                              int32_t* topk_idx_out, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* Execution status of the last dsa_fused_forward on workspace `ws`:
+ * synchronises `stream` (the stream that call used), then returns
+ * DSA_ERR_EXEC if that call was a single-launch decode and one of its waits
+ * between workgroups gave up (its results are not valid; see Co-residency),
+ * DSA_ERR_HIP if the synchronisation or the read-back failed, else DSA_OK.
+ * Other launch kinds have no waits and always report DSA_OK here.  Host
+ * call; blocks until the stream is idle. */
+dsa_status dsa_exec_status(const void* ws, void* stream);
+
+/* Number of polls a wait between decode workgroups makes before it gives up
+ * (default 16777216, i.e. seconds).  0 makes every such wait give up at
+ * once: the failure path is then exercised deterministically (used by the
+ * tests).  Process-wide; applies to launches enqueued after the call. */
+void dsa_set_wait_limit(uint32_t polls);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* dsa_last_error(void);

@@ -173,20 +173,6 @@ def forward(params, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[int]]
     return out, idx
 
 
-def top_k_rows(params, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[int]] = None,
-               batches: Optional[Sequence[int]] = None) -> np.ndarray:
-    """Indexer + top-k only, for the chosen (batch, row) pairs: [nb, nr, K]."""
-    bs = list(range(params.batch)) if batches is None else list(batches)
-    ns = list(range(params.n_q)) if rows is None else list(rows)
-    idx = np.zeros((len(bs), len(ns), params.top_k), dtype=np.int64)
-    for i, b in enumerate(bs):
-        for r, n in enumerate(ns):
-            vis = visible_count(n, params.n_q, params.kv_len)
-            idx[i, r] = select_top_k(indexer_scores(inputs["q_idx"][b, n], inputs["k_idx"][b], vis),
-                                     params.top_k)
-    return idx
-
-
 def dense_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                            softmax_scale: Optional[float] = None) -> np.ndarray:
     """Full causal attention for one sequence, written independently.

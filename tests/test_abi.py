@@ -25,8 +25,11 @@ MISALIGNED = FAKE + 4
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     declared = B.header_symbols()
-    assert set(declared) == {"dsa_workspace_size", "dsa_indexer_scores", "dsa_topk",
-                             "dsa_sparse_attn", "dsa_fused_forward", "dsa_last_error"}
+    assert {"dsa_workspace_size", "dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn",
+            "dsa_fused_forward", "dsa_exec_status", "dsa_set_wait_limit",
+            "dsa_last_error"} <= set(declared)
+    # the binding marshals exactly what the header declares
+    assert set(declared) == set(B._SIGNATURES)
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -119,3 +122,12 @@ def test_binding_raises_dsa_error():
     with pytest.raises(B.DsaError) as ei:
         B.dsa_workspace_size(_p(top_k=-3))
     assert ei.value.status == B.DSA_ERR_INVALID_ARG
+
+
+def test_exec_status_without_a_decode_launch():
+    """dsa_exec_status needs a workspace; one that no decode launch used has
+    nothing to report (and needs no device to say so)."""
+    lib = B.lib()
+    assert lib.dsa_exec_status(None, None) == B.DSA_ERR_INVALID_ARG
+    assert "null" in lib.dsa_last_error().decode()
+    assert lib.dsa_exec_status(FAKE, None) == B.DSA_OK

@@ -124,7 +124,12 @@ def test_elastic_prefill_64k_sampled_rows(announce):
     assert 0 < x["route"].sum() < x["route"].size     # both routes present
     announce(f"fused_forward {w}")
     out, idx = run_fused(w, x)
-    rows = synth.sample_rows(w, 12).tolist()
+    # every index row of every sequence that has a sparse head
+    sparse_seqs = [b for b in range(w.batch) if x["route"][b].any()]
+    check_index_structure(w, idx, batches=sparse_seqs)
+    # fixed rows (start, K boundary, end) plus 64 uniform rows of the interior
+    rows = synth.sample_rows(w, 64).tolist()
+    assert sum(2056 < r < w.n_q - 16 for r in rows) >= 60
     announce(f"oracle on {len(rows)} sampled rows x 2 sequences")
     check_rows(w, x, out, idx, rows=rows)
     del out, idx
@@ -282,6 +287,80 @@ def test_deterministic_repeat(announce):
     o3, i3 = run_fused(w, x)
     assert torch.equal(o1, o2) and torch.equal(o1, o3)
     assert torch.equal(i1, i2) and torch.equal(i1, i3)
+
+
+def run_entry_points(w, x):
+    """The same forward through the three separate entry points (other
+    kernels, other work split): scores, then top-k, then attention."""
+    p = B.problem_for(w)
+    dev = to_device(w, x)
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((w.batch, w.n_q, w.kv_len), dtype=torch.float32, device="cuda")
+    idx = torch.full((w.batch, w.n_q, w.top_k), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q, w.h_q, w.head_dim), dtype=torch.float32, device="cuda")
+    B.dsa_indexer_scores(p, dev["q_idx"], dev["k_idx"], scores)
+    B.dsa_topk(p, scores, idx, ws)
+    B.dsa_sparse_attn(p, dev["q"], dev["k"], dev["v"], idx, dev["gate"], dev["y2"], dev["route"],
+                      out, ws)
+    torch.cuda.synchronize()
+    return out, idx
+
+
+PLANS = [("decode_b8_ctx40k", synth.WORKLOADS["decode_b8_ctx128k"].replace(kv_len=40000)),
+         ("decode_mqa_ctx200k", synth.WORKLOADS["decode_ctx1m_mqa"].replace(kv_len=200000)),
+         ("prefill_3k_mixed_route", _w(2, 3000, 3000, 8, 2, 128, 64, 512, route_p=0.6, seed=31))]
+
+
+@pytest.mark.parametrize("name,w", PLANS, ids=[p[0] for p in PLANS])
+def test_same_result_under_another_plan(name, w, announce):
+    """A race or an order-dependent reduction would show as a difference
+    between two different work splits of the same problem: the fused call
+    (one decode launch, or chunked prefill launches) against the separate
+    entry points.  Index rows must agree bit for bit, outputs within the
+    float tolerance (both are also compared with the oracle on some rows)."""
+    x = synth.make_inputs(w)
+    announce(f"fused_forward vs entry points {name} {w}")
+    o1, i1 = run_fused(w, x)
+    o2, i2 = run_entry_points(w, x)
+    assert torch.equal(i1, i2)
+    assert torch.max(torch.abs(o1 - o2)).item() <= TOL[w.qkv_dtype]
+    rows = [0] if w.n_q == 1 else synth.sample_rows(w, 8).tolist()
+    check_rows(w, x, o2, i2, rows=rows)
+
+
+def test_decode_give_up_is_reported(announce):
+    """A wait between decode workgroups that gives up must reach the caller:
+    with a wait limit of 0 every wait gives up at once (every kernel still
+    exits normally), the outputs are NaN, the index rows -1, and
+    dsa_exec_status reports DSA_ERR_EXEC.  The next launch on the same
+    workspace, with the default limit, is correct again."""
+    w = synth.WORKLOADS["decode_b8_ctx128k"].replace(kv_len=30000)
+    x = synth.make_inputs(w)
+    p = B.problem_for(w)
+    dev = to_device(w, x)
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    out = torch.zeros((w.batch, 1, w.h_q, w.head_dim), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((w.batch, 1, w.top_k), dtype=torch.int32, device="cuda")
+
+    def fwd():
+        B.dsa_fused_forward(p, dev["q_idx"], dev["k_idx"], dev["q"], dev["k"], dev["v"],
+                            dev["gate"], dev["y2"], dev["route"], out, idx, ws)
+
+    announce("decode with wait limit 0")
+    B.dsa_set_wait_limit(0)
+    try:
+        fwd()
+        with pytest.raises(B.DsaError) as ei:
+            B.dsa_exec_status(ws)
+        assert ei.value.status == B.DSA_ERR_EXEC
+    finally:
+        B.dsa_set_wait_limit(1 << 24)
+    assert torch.all(torch.isnan(out)).item()
+    assert torch.all(idx == -1).item()
+    announce("decode again with the default limit")
+    fwd()
+    B.dsa_exec_status(ws)      # raises on failure
+    check_rows(w, x, out, idx, rows=[0])
 
 
 # --------------------------------------------------------------------------- single entry points

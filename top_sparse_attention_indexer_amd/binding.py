@@ -15,10 +15,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdsa.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "dsa.h")
 
-DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP, DSA_ERR_EXEC = range(6)
 DSA_FP32, DSA_BF16 = 0, 1
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
-                3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
+                3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP", 5: "DSA_ERR_EXEC"}
 
 
 class DsaProblem(ctypes.Structure):
@@ -46,6 +46,8 @@ _SIGNATURES = {
                                        ctypes.c_size_t, _vp]),
     "dsa_fused_forward": (ctypes.c_int, [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, ctypes.c_size_t, _vp]),
+    "dsa_exec_status": (ctypes.c_int, [_vp, _vp]),
+    "dsa_set_wait_limit": (None, [ctypes.c_uint32]),
     "dsa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -143,6 +145,15 @@ def dsa_fused_forward(p, q_idx, k_idx, q, k, v, gate, y2, route, out, topk_idx_o
     _check(lib().dsa_fused_forward(ctypes.byref(p), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(gate), _ptr(y2), _ptr(route), _ptr(out),
                                    _ptr(topk_idx_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def dsa_exec_status(ws, stream=None):
+    """Raises DsaError(DSA_ERR_EXEC) if the last fused forward on ``ws`` gave up."""
+    _check(lib().dsa_exec_status(_ptr(ws), _stream(stream)))
+
+
+def dsa_set_wait_limit(polls: int):
+    lib().dsa_set_wait_limit(int(polls))
 
 
 def dsa_last_error() -> str:

@@ -44,6 +44,7 @@
 //       applies the gate.
 #include <unistd.h>
 
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <map>
@@ -80,6 +81,7 @@ struct DecodeArgs {
   uint64_t* fcand;   // [rows][Cpad] each chunk's M largest order values, in position order
   uint64_t* sgslot;  // [B][ngroups][8] epoch-tagged group slots of the sequence barriers
   uint64_t* verdict; // [B][8] epoch-tagged: 1 = candidates hold the top K, 2 = they may not
+  uint64_t* seqerr;  // [B][8] epoch-tagged: 1 = a unit of the sequence gave up waiting
   int B, N, L, Hq, Hkv, K, CH, nch, S, nhc, cand_cap;
   uint64_t* fstat;   // [rows][nch][4 waves][2]: (largest | smallest << 32) candidate key of
                      // the wave's share of the chunk, and the chunk's (M+1)-th value
@@ -87,6 +89,7 @@ struct DecodeArgs {
   int ccnt;          // candidates present per row
   float scale_log2;
   uint32_t epoch;    // distinct per launch; tags every control word
+  uint32_t spin_limit;  // polls before a wait gives up (0: give up at the first wait)
 };
 
 __device__ __forceinline__ bool seq_sparse(const uint8_t* route, int b, int Hq) {
@@ -131,18 +134,29 @@ __device__ __forceinline__ bool tagged(uint64_t v, uint32_t epoch, uint32_t at_l
   return (uint32_t)(v >> 32) == epoch && (uint32_t)v >= at_least;
 }
 
-__device__ __forceinline__ void raise_error(const DecodeArgs& a) {
-  st_dev64(a.ctl, ((uint64_t)a.epoch << 32) | 1ull);
+__device__ __forceinline__ void raise_error(const DecodeArgs& a, int b) {
+  const uint64_t tag = ((uint64_t)a.epoch << 32) | 1ull;
+  st_dev64(a.seqerr + 8 * b, tag);
+  st_dev64(a.ctl, tag);
 }
 
-// Bounded wait of one thread for a tagged word; false on timeout or error.
-__device__ __forceinline__ bool wait_tag(const DecodeArgs& a, const uint64_t* p, uint32_t at_least) {
+// Bounded wait of one thread for a tagged word of sequence b; false when the
+// wait gives up (after spin_limit polls, at once when spin_limit is 0) or
+// when another unit of the sequence already gave up.  A give-up is recorded
+// in the sequence's abort word and in the launch's error word (control word
+// 0), which the host reads back through dsa_exec_status.
+__device__ __forceinline__ bool wait_tag(const DecodeArgs& a, int b, const uint64_t* p,
+                                         uint32_t at_least) {
+  if (a.spin_limit == 0) {
+    raise_error(a, b);
+    return false;
+  }
   uint32_t spins = 0;
   while (!tagged(ld_dev64(p), a.epoch, at_least)) {
-    if (tagged(ld_dev64(a.ctl), a.epoch, 1u)) return false;
+    if (tagged(ld_dev64(a.seqerr + 8 * b), a.epoch, 1u)) return false;
     __builtin_amdgcn_s_sleep(1);
-    if (++spins > (1u << 24)) {
-      raise_error(a);
+    if (++spins > a.spin_limit) {
+      raise_error(a, b);
       return false;
     }
   }
@@ -174,13 +188,13 @@ __device__ __forceinline__ bool seq_sync(const DecodeArgs& a, int b, uint32_t ph
   __syncthreads();
   if (lu == gi * kBarGroup) {
     const int gsize = min(kBarGroup, a.nch - gi * kBarGroup);
-    if ((int)threadIdx.x < gsize && !wait_tag(a, mslot + u0 + gi * kBarGroup + threadIdx.x, phase))
+    if ((int)threadIdx.x < gsize && !wait_tag(a, b, mslot + u0 + gi * kBarGroup + threadIdx.x, phase))
       *flag = 0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0 && *flag) st_dev64(gslot + 8 * gi, tag);
   }
-  if ((int)threadIdx.x < ngs && !wait_tag(a, gslot + 8 * threadIdx.x, phase)) *flag = 0;
+  if ((int)threadIdx.x < ngs && !wait_tag(a, b, gslot + 8 * threadIdx.x, phase)) *flag = 0;
   __syncthreads();
   return *flag != 0;
 }
@@ -213,9 +227,23 @@ __device__ __forceinline__ bool rows_ready(const DecodeArgs& a, int b, int* flag
   __syncthreads();
   if (threadIdx.x == 0) *flag = 1;
   __syncthreads();
-  if ((int)threadIdx.x < a.N && !wait_tag(a, a.rowtag + b * a.N + threadIdx.x, 2u)) *flag = 0;
+  if ((int)threadIdx.x < a.N && !wait_tag(a, b, a.rowtag + b * a.N + threadIdx.x, 2u)) *flag = 0;
   __syncthreads();
   return *flag != 0;
+}
+
+// A unit that gave up waiting leaves its sequence's results undefined: it
+// marks them so (NaN outputs, index rows of -1) before it returns.  Units of
+// the sequence cannot pass the wait it gave up at, so no valid result of the
+// sequence is written after these.
+template <int HD>
+__device__ void abandon(const DecodeArgs& a, int b) {
+  const size_t n_out = (size_t)a.N * a.Hq * HD;
+  float* o = a.out + (size_t)b * n_out;
+  const float qnan = __uint_as_float(0x7fc00000u);
+  for (size_t i = threadIdx.x; i < n_out; i += DT) o[i] = qnan;
+  int32_t* l = a.list + (size_t)b * a.N * a.K;
+  for (size_t i = threadIdx.x; i < (size_t)a.N * a.K; i += DT) l[i] = -1;
 }
 
 // kk-th largest (from the top) over hist[0..nb): bin and count above it.
@@ -909,7 +937,10 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
     if (threadIdx.x == 0) res[2] = 0;
   }
   // the sequence's per-row accumulators are cleared by its first unit
-  if (!rows_ready(a, b, &flag)) return;
+  if (!rows_ready(a, b, &flag)) {
+    abandon<HD>(a, b);
+    return;
+  }
 
   // ------------------------------------------------ histogram selection phases
   // H1: first-digit (top 11 key bits) histogram of every row -> global.
@@ -1407,7 +1438,10 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       }
       for (int o = (int)base + (int)threadIdx.x; o < a.M; o += DT) st_dev64(cw + o, 0ull);
     }
-    if (!seq_sync(a, b, ph++, &flag)) return;
+    if (!seq_sync(a, b, ph++, &flag)) {
+      abandon<HD>(a, b);
+      return;
+    }
     // C2: every unit with an attention item loads the row's candidates,
     // counting their first digit as they arrive, and finds their K-th
     // largest value cK.  The candidates hold the row's top K when cK is above
@@ -1533,22 +1567,31 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       // sequence falls back (unit 0 publishes the verdict)
       if (threadIdx.x == 0) {
         res[0] = 0;
-        if (wait_tag(a, a.verdict + 8 * b, 1u)) res[0] = (uint32_t)ld_dev64(a.verdict + 8 * b);
+        if (wait_tag(a, b, a.verdict + 8 * b, 1u)) res[0] = (uint32_t)ld_dev64(a.verdict + 8 * b);
       }
       __syncthreads();
       const uint32_t vd = res[0];
       __syncthreads();
+      if (vd == 0u) abandon<HD>(a, b);   // the wait gave up
       if (vd != 2u) return;
       slow = true;
     }
   }
   if (slow) {
     build_hist0();
-    if (!seq_sync(a, b, ph++, &flag)) return;
-    cand_phase();
-    if (!seq_sync(a, b, ph++, &flag)) return;
-    select_phase();
-    if (!seq_sync(a, b, ph++, &flag)) return;
+    bool ok = seq_sync(a, b, ph++, &flag);
+    if (ok) {
+      cand_phase();
+      ok = seq_sync(a, b, ph++, &flag);
+    }
+    if (ok) {
+      select_phase();
+      ok = seq_sync(a, b, ph++, &flag);
+    }
+    if (!ok) {
+      abandon<HD>(a, b);
+      return;
+    }
     llist = nullptr;
   }
   for (int il = c; il < items_seq; il += a.nch) run_item(b * items_seq + il, llist);
@@ -1670,7 +1713,7 @@ size_t decode_ws_bound(const Dims& D) {
 // words, both digit histograms, candidate counts, tickets), then per-chunk
 // counts, candidates and attention partials.
 struct DecodeLayout {
-  size_t ctl, rowtag, sgslot, verdict, hist0, hist1, cand_n, ticket, cnt, cand, fcand, fstat,
+  size_t ctl, rowtag, sgslot, verdict, seqerr, hist0, hist1, cand_n, ticket, cnt, cand, fcand, fstat,
       part, total;
 };
 
@@ -1683,6 +1726,7 @@ DecodeLayout decode_layout(const Dims& D, const DecodePlan& P) {
   Lo.rowtag = off; off = al(off + rows * 8);
   Lo.sgslot = off; off = al(off + (size_t)D.B * ((P.nch + kBarGroup - 1) / kBarGroup) * 64);
   Lo.verdict = off; off = al(off + (size_t)D.B * 64);
+  Lo.seqerr = off; off = al(off + (size_t)D.B * 64);
   Lo.hist0 = off;  off = al(off + rows * 2048 * 4);
   Lo.hist1 = off;  off = al(off + rows * 2048 * 4);
   Lo.cand_n = off; off = al(off + rows * kCandGroups * 4);
@@ -1724,6 +1768,44 @@ StreamOrder& stream_order(int dev) {
   return orders[dev & 63];
 }
 
+// Polls a decode wait makes before it gives up; see dsa_set_wait_limit.
+std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
+
+// Epoch of the last decode launch per workspace (its control block sits at
+// the workspace's start), so that dsa_exec_status can tell this launch's
+// error word from one left by an earlier launch.
+std::mutex g_ws_mu;
+std::map<const void*, uint32_t> g_ws_epoch;
+
+void record_launch(const void* ws, uint32_t epoch) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  g_ws_epoch[ws] = epoch;
+}
+
+void set_wait_limit(uint32_t polls) { g_wait_limit.store(polls, std::memory_order_relaxed); }
+
+int decode_exec_status(const void* ws, hipStream_t s, hipError_t* err) {
+  *err = hipSuccess;
+  uint32_t epoch = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto it = g_ws_epoch.find(ws);
+    if (it == g_ws_epoch.end()) return 0;
+    epoch = it->second;
+  }
+  *err = hipStreamSynchronize(s);
+  if (*err != hipSuccess) return 0;
+  uint64_t word = 0;
+  *err = hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost);
+  if (*err != hipSuccess) return 0;
+  return word == (((uint64_t)epoch << 32) | 1ull) ? 1 : 0;
+}
+
+void forget_launch(const void* ws) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  g_ws_epoch.erase(ws);
+}
+
 hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, const void* k_idx,
                          const void* q, const void* k, const void* v, const float* gate,
                          const float* y2, const uint8_t* route, float* out, int32_t* list,
@@ -1745,6 +1827,7 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   a.fcand = (uint64_t*)(w + Lo.fcand);
   a.sgslot = (uint64_t*)(w + Lo.sgslot);
   a.verdict = (uint64_t*)(w + Lo.verdict);
+  a.seqerr = (uint64_t*)(w + Lo.seqerr);
   a.M = P.M; a.Cpad = P.Cpad;
   a.ccnt = P.M ? (P.nch - 1) * P.M + std::min(D.L - (P.nch - 1) * P.CH, P.M) : 0;
   a.fstat = (uint64_t*)(w + Lo.fstat);
@@ -1766,6 +1849,8 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
     if (e != hipSuccess) return e;
   }
   a.epoch = next_epoch(so);
+  a.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
+  record_launch(ws, a.epoch);
   void* args[] = {&a};
   // the completion event rides on the kernel's own dispatch
   e = hipExtLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s, nullptr, so.done, 0);

@@ -321,11 +321,13 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   if (P.fused_decode) {
+    // the decode control block (and its error word) sits at the workspace start
     int32_t* list = topk_idx_out ? topk_idx_out : (int32_t*)(w + P.idx_off);
     return hip_status(dsa::launch_decode(D, P.dp, q_idx, k_idx, q, k, v, gate, y2, route, out,
                                          list, w + P.dec_off, s),
                       "dsa_fused_forward");
   }
+  dsa::forget_launch(ws);
   float* scores = (float*)(w + P.scores_off);
   int32_t* idx_chunk = (int32_t*)(w + P.idx_off);
   float* part = P.part_bytes ? (float*)(w + P.part_off) : nullptr;
@@ -376,6 +378,20 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
   }
   return hip_status(e, "dsa_fused_forward");
 }
+
+dsa_status dsa_exec_status(const void* ws, void* stream) {
+  if (!ws) return fail(DSA_ERR_INVALID_ARG, "workspace is null");
+  hipError_t e;
+  const int gave_up = dsa::decode_exec_status(ws, (hipStream_t)stream, &e);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "dsa_exec_status: %s", hipGetErrorString(e));
+  if (gave_up)
+    return fail(DSA_ERR_EXEC,
+                "the last decode launch on this workspace gave up waiting for its workgroups "
+                "(other work kept some of them from running); its outputs are NaN");
+  return ok();
+}
+
+void dsa_set_wait_limit(uint32_t polls) { dsa::set_wait_limit(polls); }
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
 

@@ -67,6 +67,22 @@ hipError_t launch_attention(const Dims& D, const AttnArgs& a, hipStream_t s);
 bool mfma_attention_supported(const Dims& D);
 hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& a, hipStream_t s);
 
+// bf16 MFMA attention blocked by key range (prefill): both routes in one
+// persistent launch whose workgroups take (sequence, KV head, key range)
+// slices XCD by XCD, per-range partials merged afterwards.  Needs
+// slice_ws_bytes(D, R) of workspace for a launch over R query rows, and index
+// rows that are ascending in their valid entries (as dsa_topk writes them).
+constexpr int kSliceKeys = 4096;    // keys per range
+struct SlicePlan {
+  int RC = 0;    // keys per range
+  int NC = 0;    // ranges of the longest row
+  int cap = 0;   // slices per XCD queue table
+};
+SlicePlan slice_plan(const Dims& D, int R);
+size_t slice_ws_bytes(const Dims& D, int R);
+bool slice_attention_supported(const Dims& D);
+hipError_t launch_attention_slices(const Dims& D, const AttnArgs& a, void* ws, hipStream_t s);
+
 // ---- fused decode (one cooperative launch) ----------------------------------
 struct DecodePlan {
   int grid = 0;      // co-resident workgroups
@@ -89,6 +105,16 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
                          const void* q, const void* k, const void* v, const float* gate,
                          const float* y2, const uint8_t* route, float* out, int32_t* list,
                          void* ws, hipStream_t s);
+
+// Failure reporting of the decode kernel: every wait between its workgroups
+// is bounded by a number of polls (kDefaultWaitLimit unless changed; 0 makes
+// every wait give up at once).  decode_exec_status synchronises `s` and
+// returns 1 if the last decode launch on workspace `ws` gave up, else 0
+// (also when no decode launch used `ws`); forget_launch drops that record.
+constexpr uint32_t kDefaultWaitLimit = 1u << 24;
+void set_wait_limit(uint32_t polls);
+int decode_exec_status(const void* ws, hipStream_t s, hipError_t* err);
+void forget_launch(const void* ws);
 
 // ---- misc ------------------------------------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s);

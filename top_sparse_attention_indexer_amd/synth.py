@@ -158,12 +158,11 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
 def sample_rows(w: Workload, count: int, seed: int = 7) -> np.ndarray:
     """A seeded, stratified sample of query rows (n indices, ascending).
 
-    Covers the first rows, the rows around the point where the visible length
-    crosses K, the last rows and a uniform draw of the rest.
+    The first 16 rows, the 17 rows around the point where the visible length
+    crosses K, the last 16 rows, plus ``count`` further rows drawn uniformly
+    from the rest (all rows when the workload has no more).
     """
     N = w.n_q
-    if count >= N:
-        return np.arange(N, dtype=np.int64)
     first_vis = w.kv_len - N + 1            # visible keys of query row 0
     cross = w.top_k - first_vis             # row whose visible length is K + 1
     picks = set(range(min(16, N)))
@@ -171,8 +170,8 @@ def sample_rows(w: Workload, count: int, seed: int = 7) -> np.ndarray:
     for r in range(cross - 8, cross + 9):
         if 0 <= r < N:
             picks.add(r)
+    rest = np.setdiff1d(np.arange(N), np.fromiter(picks, dtype=np.int64))
     rng = np.random.Generator(np.random.PCG64(seed))
-    rest = max(0, count - len(picks))
-    if rest:
-        picks.update(rng.choice(N, size=min(rest, N), replace=False).tolist())
-    return np.array(sorted(picks)[:max(count, len(picks))], dtype=np.int64)
+    if count > 0 and rest.size:
+        picks.update(rng.choice(rest, size=min(count, rest.size), replace=False).tolist())
+    return np.array(sorted(picks), dtype=np.int64)
