@@ -111,6 +111,7 @@ def main():
     ap.add_argument("--workload", default="decode_b8_ctx128k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", action="store_true", help="print per-stage GPU time")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the workload, copy this many bytes device to device "
                          "(a plain copy kernel of known size, for counter calibration)")
@@ -169,6 +170,14 @@ def main():
         b_.record(stream)
     torch.cuda.synchronize()
     per = np.array([a.elapsed_time(b_) for a, b_ in ev])
+    if args.stages:
+        B.dsa_profile_start(1 << 16)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        st, dropped = B.dsa_profile_stop()
+        print(json.dumps({k: [v[0] / args.steps, v[1] / args.steps] for k, v in st.items()}),
+              file=sys.stderr)
     tokens = w.batch * w.n_q
     byt, flops = algorithmic_work(w, x["route"])
     achieved = byt / (ms / 1e3) / 1e9

@@ -155,6 +155,22 @@ dsa_status dsa_exec_status(const void* ws, void* stream);
  * tests).  Process-wide; applies to launches enqueued after the call. */
 void dsa_set_wait_limit(uint32_t polls);
 
+/* Stage timing (tracing).  Between dsa_profile_start and dsa_profile_stop,
+ * every kernel the entry points enqueue is bracketed by two HIP events on its
+ * launch stream (up to max_launches launches; later ones are counted as
+ * dropped).  dsa_profile_stop synchronises on those events and returns, per
+ * stage, the summed GPU time in milliseconds and the number of launches:
+ *   0 indexer scores, 1 top-k selection, 2 attention (both routes),
+ *   3 merge of split/range partials, 4 single-launch decode (the whole
+ *   path), 5 preparation (range offsets, work queues).
+ * ms and launches have n_stages entries (either may be NULL); dropped
+ * (nullable) receives the count of launches not timed.  Host calls; the
+ * events are created by start and destroyed by stop. */
+#define DSA_PROFILE_STAGES 6
+dsa_status dsa_profile_start(int32_t max_launches);
+dsa_status dsa_profile_stop(double* ms, int32_t* launches, int32_t n_stages,
+                            int64_t* dropped);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* dsa_last_error(void);
 

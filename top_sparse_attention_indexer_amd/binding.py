@@ -48,6 +48,10 @@ _SIGNATURES = {
                                          _vp, ctypes.c_size_t, _vp]),
     "dsa_exec_status": (ctypes.c_int, [_vp, _vp]),
     "dsa_set_wait_limit": (None, [ctypes.c_uint32]),
+    "dsa_profile_start": (ctypes.c_int, [ctypes.c_int32]),
+    "dsa_profile_stop": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_int64)]),
     "dsa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -154,6 +158,24 @@ def dsa_exec_status(ws, stream=None):
 
 def dsa_set_wait_limit(polls: int):
     lib().dsa_set_wait_limit(int(polls))
+
+
+STAGES = ("indexer", "topk", "attention", "merge", "decode", "prep")
+
+
+def dsa_profile_start(max_launches: int = 65536):
+    _check(lib().dsa_profile_start(int(max_launches)))
+
+
+def dsa_profile_stop():
+    """{stage: (milliseconds, launches)} summed since dsa_profile_start, and the
+    count of launches that were not timed."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    dropped = ctypes.c_int64(0)
+    _check(lib().dsa_profile_stop(ms, cnt, n, ctypes.byref(dropped)))
+    return {STAGES[i]: (ms[i], cnt[i]) for i in range(n)}, dropped.value
 
 
 def dsa_last_error() -> str:

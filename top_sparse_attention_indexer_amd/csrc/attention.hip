@@ -260,6 +260,7 @@ hipError_t attn_launch(const Dims& D, const AttnArgs& a, hipStream_t s) {
     if (mode == 1 && !a.route) break;
     const int splits = mode ? a.splits_dense : a.splits_sparse;
     const size_t blocks = items * splits;
+    ProfScope ps(s, kStageAttention);
     hipLaunchKernelGGL((k_attn<T, HD>), dim3((unsigned)blocks), dim3(AT), 0, s, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, a.topk, a.idx_rows_per_b, a.idx_n_base,
                        a.gate, a.y2, a.route, a.out, a.part, D.N, D.L, D.Hq, D.Hkv, D.K, a.n0, a.R,
@@ -267,6 +268,7 @@ hipError_t attn_launch(const Dims& D, const AttnArgs& a, hipStream_t s) {
   }
   if (stride > 1) {
     const size_t blocks = (size_t)D.B * a.R * D.Hq;
+    ProfScope ps(s, kStageMerge);
     hipLaunchKernelGGL((k_attn_merge<HD>), dim3((unsigned)blocks), dim3(HD), 0, s, a.part, a.gate,
                        a.y2, a.route, a.out, D.N, D.Hq, a.n0, a.R, a.splits_sparse,
                        a.route ? a.splits_dense : 1, stride);

@@ -28,14 +28,12 @@
 #include "common.h"
 #include "launch.h"
 #include "mfma.h"
+#include "attn_tile.h"
 
 namespace dsa {
 namespace {
 
 constexpr int MT = 256;          // threads (4 waves)
-constexpr int VSTR = 288;        // LDS row stride of a 32 x d value tile (bytes)
-constexpr int KSTR = 272;        // LDS row stride of a 32 x d key tile (bytes)
-constexpr float kLog2e = 1.4426950408889634f;
 
 struct MfmaArgs {
   const bf16_bits* q; const bf16_bits* k; const bf16_bits* v;
@@ -49,70 +47,6 @@ struct MfmaArgs {
   int sgpl;           // sparse tokens: KV heads per item (a divisor of Hkv)
   float scale_log2;
 };
-
-// Shared per-step core: given this wave's two 16-key halves (A operands for
-// S^T already loaded), the 32 x d value tile in LDS, update the running
-// state of the lane's column.
-template <int HD>
-struct ColState {
-  float m, l;
-  f32x4 o[HD / 16];
-};
-
-template <int HD>
-__device__ __forceinline__ void step_core(const uint4 (&ka)[2][HD / 32], const bf16x8 (&qb)[HD / 32],
-                                          const bool (&kvalid)[2][4], const char* vtile,
-                                          float scale_log2, ColState<HD>& st) {
-  constexpr int T = HD / 32;
-  const int lane = threadIdx.x & 63;
-  const int q = lane >> 4, i = lane & 15;
-  float s[8];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[u][t]), qb[t], acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[u * 4 + r] = kvalid[u][r] ? acc[r] * scale_log2 : -INFINITY;
-  }
-  float mt = s[0];
-#pragma unroll
-  for (int x = 1; x < 8; ++x) mt = fmaxf(mt, s[x]);
-  mt = max_xor16(mt);
-  mt = max_xor32(mt);
-  const float mnew = fmaxf(st.m, mt);
-  float alpha = 1.f;
-  float p[8];
-  if (mnew == -INFINITY) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) p[x] = 0.f;
-  } else {
-    alpha = exp2_fast(st.m - mnew);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) p[x] = exp2_fast(s[x] - mnew);
-  }
-  float ps = 0.f;
-#pragma unroll
-  for (int x = 0; x < 8; ++x) ps += p[x];
-  st.l = st.l * alpha + ps;  // this lane's keys only; summed over quads at the end
-  st.m = mnew;
-  const bf16x8 pb = pack8(p);
-  // value tile rows: first half keys 4q+k, second half 16+4q+k; this lane
-  // (4k + c within its 16-lane group) points at row 4q + i/4, dims 4*(i%4)
-  const int row0 = 4 * q + (i >> 2);
-  const int colb = (i & 3) * 8;  // bytes
-#pragma unroll
-  for (int dt = 0; dt < HD / 16; ++dt) {
-    const uint2 lo = lds_tr(vtile, row0 * VSTR + dt * 32 + colb);
-    const uint2 hi = lds_tr(vtile, (16 + row0) * VSTR + dt * 32 + colb);
-    uint4 u;
-    u.x = lo.x; u.y = lo.y; u.z = hi.x; u.w = hi.y;
-    f32x4 o = st.o[dt];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] *= alpha;
-    st.o[dt] = mfma16(as_bf16x8(u), pb, o);
-  }
-}
 
 // Final normalisation, gate and store of one column (lane owns column i; the
 // four quads hold dims 16*dt + 4q + r).
@@ -502,6 +436,7 @@ hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& aa, hipStream_t 
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int work = (dense_max > 0 ? kDenseWork : 0) | (aa.skip_sparse ? 0 : kSparseWork);
   const dim3 g((unsigned)blocks), t(MT);
+  ProfScope ps(s, kStageAttention);
 #define DSA_ATTN_MFMA(HDV)                                                                  \
   if (work == kDenseWork) hipLaunchKernelGGL((k_attn_mfma<HDV, kDenseWork>), g, t, 0, s, a); \
   else if (work == kSparseWork)                                                            \

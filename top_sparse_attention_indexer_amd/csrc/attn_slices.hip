@@ -1,0 +1,711 @@
+// Prefill attention for both routes in one launch, blocked by key range so
+// that the keys and values a group of workgroups gathers stay in one XCD's L2.
+//
+// What it computes: for a sparse head, softmax(q k^T * scale) v over the
+// selected rows of the query token ("混合注意力架构演进：从线性注意力到稀疏门控
+// 的技术权衡" §三; steps 3-4 of the gated forward on "超大规模MoE架构中稀疏注意力
+// 机制的演进与实践" §四.1); for a dense head the same over every visible key
+// ("Advanced Attention Mechanisms" article §2.1), both followed by the gate
+// blend of step 5.  The page "Elastic Attention：动态路由优化大模型长文本处理"
+// §3.1 puts both kinds of head in one fused op with load balancing by the
+// actual route; here they are items of one persistent grid.
+//
+// Why key ranges.  A sparse token reads 2048 scattered 256-byte key and value
+// rows per KV head; gathered from a whole 65536-token sequence they come from
+// HBM / the Infinity Cache (about 7.5-8.7 TB/s on MI355X), while gathered from
+// a region that fits one XCD's 4 MB L2 they come at about 27 TB/s (measured
+// with a plain gather kernel).  So the keys are cut into ranges of RC
+// positions and the work into slices (sequence, KV head, range): the K/V of
+// one slice (RC * d * 4 bytes; 2 MB for RC = 4096, d = 128) is what the
+// workgroups of an XCD gather from while they work through that slice.
+// Every (query row, head) gets one partial result per range it sees (its
+// online-softmax state: log2-sum-exp and normalised output), merged by
+// k_merge_ranges; rows that see a single range write the output directly.
+//
+// Scheduling.  k_sched lists the non-empty slices in (sequence, KV head,
+// range) order and deals them to the 8 XCDs round robin; each XCD has a
+// queue of items (dense query tiles and sparse query blocks of its slices,
+// the two kinds interleaved evenly within a slice so that MFMA-bound and
+// gather-bound work run side by side).  The attention grid is persistent:
+// each workgroup reads its XCD id from the hardware register and takes items
+// from that XCD's queue with an atomic counter, then from the other queues
+// once its own is empty.  The mapping only decides cache locality; every item
+// is taken exactly once whatever XCD a workgroup runs on.
+#include "attn_tile.h"
+#include "common.h"
+#include "launch.h"
+#include "mfma.h"
+
+namespace dsa {
+namespace {
+
+constexpr int ST = 256;             // threads (4 waves)
+constexpr int kXcd = 8;             // XCDs (queues)
+constexpr int kQB = 16;             // query rows per sparse item
+constexpr int DROWS = 128;          // query rows per dense tile
+constexpr int DKEYS = 64;           // keys per dense step
+constexpr int kDenseLds = 4 * DKEYS * 256;   // K and V, double-buffered, 64 rows of <= 256 B
+constexpr int kSeg = 256;           // index entries staged per wave at a time
+constexpr int kSparseLds = 4 * 2 * 32 * 256 + 4 * kSeg * 4;   // per wave: key and value tiles, entries
+constexpr int kLds = kDenseLds > kSparseLds ? kDenseLds : kSparseLds;
+
+struct SliceArgs {
+  const bf16_bits* q; const bf16_bits* k; const bf16_bits* v;
+  const int32_t* topk; int idx_rows_per_b, idx_n_base;
+  const float* gate; const float* y2; const uint8_t* route;
+  float* out;
+  const int32_t* off;   // [B * R][NC + 1] index-row offsets of the ranges
+  const int32_t* sched; // queue tables (k_sched)
+  uint32_t* ctr;        // [kXcd] queue counters, zeroed by k_sched
+  float* part_o;        // [B * R][NC][Hq][HD] normalised partial outputs
+  float* part_lse;      // [B * R][NC][Hq] log2-sum-exp of the partials
+  int B, N, L, Hq, Hkv, K;
+  int n0, R;            // query rows [n0, n0 + R) of each sequence
+  int RC, NC;           // keys per range; ranges seen by the chunk's last row
+  int cap;              // slices per queue table
+  float scale_log2;
+};
+
+// Queue tables: [0, 8) slice counts, [8, 16) item totals, then per queue the
+// slice ids (cap each) and the exclusive prefix of their item counts.
+__device__ __forceinline__ const int32_t* q_sid(const SliceArgs& a, int x) {
+  return a.sched + 16 + (size_t)x * a.cap;
+}
+__device__ __forceinline__ const int32_t* q_pre(const SliceArgs& a, int x) {
+  return a.sched + 16 + (size_t)(kXcd + x) * a.cap;
+}
+
+// Query heads of group g of sequence b by route.
+__device__ __forceinline__ bool head_sparse(const SliceArgs& a, int b, int h) {
+  return a.route ? a.route[(size_t)b * a.Hq + h] != 0 : true;
+}
+
+struct SliceItems {
+  int r_c;      // first chunk row that sees the range
+  int nsp;      // sparse heads in the group
+  int nt;       // dense tiles per dense head
+  int n_dense;  // dense items
+  int n_sparse; // sparse items
+};
+
+__device__ __forceinline__ SliceItems slice_items(const SliceArgs& a, int b, int g, int c) {
+  SliceItems s;
+  const int G = a.Hq / a.Hkv;
+  const int off = a.L - a.N + a.n0;   // position of chunk row 0
+  s.r_c = max(0, c * a.RC - off);
+  s.nsp = 0;
+  for (int x = 0; x < G; ++x) s.nsp += head_sparse(a, b, g * G + x) ? 1 : 0;
+  if (s.r_c >= a.R) {
+    s.nt = s.n_dense = s.n_sparse = 0;
+    return s;
+  }
+  s.nt = (a.R + DROWS - 1) / DROWS - s.r_c / DROWS;
+  s.n_dense = (G - s.nsp) * s.nt;
+  s.n_sparse = s.nsp > 0 ? (a.R - s.r_c + kQB - 1) / kQB : 0;
+  return s;
+}
+
+// One workgroup: the queue tables and zeroed counters.
+__global__ __launch_bounds__(ST) void k_sched(SliceArgs a, int32_t* sched) {
+  const int lane = threadIdx.x & 63, x = threadIdx.x >> 6;
+  const int nslices = a.B * a.Hkv * a.NC;
+  // waves 0..3 take queues x and x + 4
+  for (int qx = x; qx < kXcd; qx += 4) {
+    int cnt = 0, tot = 0;
+    for (int base = qx; base < nslices; base += kXcd * 64) {
+      const int s = base + lane * kXcd;
+      int items = 0;
+      if (s < nslices) {
+        const int c = s % a.NC, bg = s / a.NC;
+        const SliceItems it = slice_items(a, bg / a.Hkv, bg % a.Hkv, c);
+        items = it.n_dense + it.n_sparse;
+      }
+      // order-preserving compaction of the non-empty slices
+      const uint64_t m = __ballot(items > 0);
+      const int rank = __popcll(m & lanemask_lt());
+      const uint32_t incl = wave_incl_scan((uint32_t)items);
+      if (items > 0) {
+        sched[16 + (size_t)qx * a.cap + cnt + rank] = s;
+        sched[16 + (size_t)(kXcd + qx) * a.cap + cnt + rank] = tot + (int)(incl - items);
+      }
+      cnt += __popcll(m);
+      tot += (int)__builtin_amdgcn_readlane((int)incl, 63);
+    }
+    if (lane == 0) {
+      sched[qx] = cnt;
+      sched[kXcd + qx] = tot;
+      a.ctr[qx] = 0u;
+    }
+  }
+}
+
+// One wave per index row: offsets of the ranges in the row.  off[c] = number
+// of valid entries (in [0, p]) below c * RC, for c = 0 .. nr (nr = p / RC + 1);
+// for ascending rows the entries of range c are [off[c], off[c + 1]).
+__global__ __launch_bounds__(ST) void k_range_offsets(SliceArgs a) {
+  __shared__ int hist[4][257];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + w;
+  if (row >= (long long)a.B * a.R) return;   // wave-uniform; no block barrier below
+  const int b = (int)(row / a.R), r = (int)(row - (long long)b * a.R);
+  const int n = a.n0 + r, p = a.L - a.N + n;
+  const int nr = p / a.RC + 1;
+  int* h = hist[w];
+  for (int c = lane; c <= nr; c += 64) h[c] = 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const int32_t* irow = a.topk + ((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.K;
+  for (int e = lane; e < a.K; e += 64) {
+    const int j = irow[e];
+    if (j >= 0 && j <= p) atomicAdd(&h[j / a.RC + 1], 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (lane == 0) {
+    int32_t* o = const_cast<int32_t*>(a.off) + (size_t)row * (a.NC + 1);
+    int run = 0;
+    for (int c = 0; c <= nr; ++c) {
+      run += h[c];
+      o[c] = run;
+    }
+  }
+}
+
+// Result of one (row, head) column: the final gated output when the row sees a
+// single range, else the partial of range c.  l is already summed over quads.
+template <int HD>
+__device__ __forceinline__ void emit_col(const SliceArgs& a, const ColState<HD>& st, float l,
+                                         int b, int r, int h, int c, int nr) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int n = a.n0 + r;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (nr == 1) {
+    const size_t orow = ((size_t)b * a.N + n) * a.Hq + h;
+    const float g = a.gate ? a.gate[orow] : 1.f;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) {
+      const int d0 = dt * 16 + 4 * q;
+      float4 v;
+      float* vv = &v.x;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        float val = st.o[dt][x] * inv;
+        if (a.gate) val = fmaf(g, val, (1.f - g) * a.y2[orow * HD + d0 + x]);
+        vv[x] = val;
+      }
+      *reinterpret_cast<float4*>(a.out + orow * HD + d0) = v;
+    }
+    return;
+  }
+  const size_t slot = (((size_t)b * a.R + r) * a.NC + c) * a.Hq + h;
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) {
+    const int d0 = dt * 16 + 4 * q;
+    float4 v = make_float4(st.o[dt][0] * inv, st.o[dt][1] * inv, st.o[dt][2] * inv,
+                           st.o[dt][3] * inv);
+    *reinterpret_cast<float4*>(a.part_o + slot * HD + d0) = v;
+  }
+  if (q == 0) a.part_lse[slot] = (l > 0.f) ? st.m + __builtin_amdgcn_logf(l) : -INFINITY;
+}
+
+// Dense query tile of a slice: 128 chunk rows of one dense head, 32 per wave as
+// two 16-column MFMA tiles, against the range's keys in 64-key steps.  Key and
+// value tiles go from memory straight into LDS (direct loads, double-buffered:
+// step s + 1 is in flight while step s computes; one barrier per step).  Rows
+// are stored back to back with their 16-byte chunks permuted so that both
+// the key reads (16 rows, one chunk) and the transposing value reads are
+// free of bank conflicts.
+template <int HD>
+__device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, char* smem) {
+  constexpr int T = HD / 32;
+  constexpr int CPR = HD / 8;                    // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                  // rows per direct load
+  constexpr int TB = DKEYS * HD * 2;             // bytes of one 64-row tile
+  char* kbuf0 = smem;
+  char* vbuf0 = smem + 2 * TB;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, i = lane & 15;
+  const int g = h / (a.Hq / a.Hkv);
+  const int rbase = tile * DROWS;
+  const int off = a.L - a.N + a.n0;              // position of chunk row 0
+  const int rlast = min(a.R - 1, rbase + DROWS - 1);
+  const int pmax = off + rlast;                  // last key any row of the tile sees
+  const int kb = c * a.RC;
+  const int ke = min(kb + a.RC, pmax + 1);       // keys [kb, ke) of the range
+  const int wlast = min(a.R - 1, rbase + w * 32 + 31);
+  const int pmax_wave = off + wlast;
+  bf16x8 qb[2][T];
+  int prow[2];
+  bool rvalid[2];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    const int r = rbase + w * 32 + cc * 16 + i;
+    rvalid[cc] = r < a.R && off + r >= kb;
+    prow[cc] = rvalid[cc] ? off + r : -1;
+    const size_t orow = ((size_t)b * a.N + a.n0 + (rvalid[cc] ? r : 0)) * a.Hq + h;
+    const bf16_bits* qr = a.q + orow * HD;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      uint4 u = rvalid[cc] ? *reinterpret_cast<const uint4*>(qr + q * (HD / 4) + t * 8)
+                           : make_uint4(0, 0, 0, 0);
+      qb[cc][t] = as_bf16x8(u);
+    }
+  }
+  ColState<HD> st[2];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    st[cc].m = -INFINITY;
+    st[cc].l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) st[cc].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const size_t rstride = (size_t)a.Hkv * HD;
+  // the 64 key and value rows from j0 into buffer buf; rows past the range
+  // read its last row (their scores are masked)
+  auto issue = [&](int j0, int buf) {
+#pragma unroll
+    for (int m = w; m < DKEYS / RPI; m += 4) {
+      const int rr = m * RPI + lane / CPR, pc = lane % CPR;
+      const size_t j = (size_t)min(j0 + rr, ke - 1);
+      const int lck = pc ^ (rr & (CPR - 1));
+      const int lcv = pc ^ ((rr & (CPR / 2 - 1)) << 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + j * rstride + lck * 8),
+                                       (__attribute__((address_space(3))) void*)(kbuf0 + buf * TB + m * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + j * rstride + lcv * 8),
+                                       (__attribute__((address_space(3))) void*)(vbuf0 + buf * TB + m * 1024),
+                                       16, 0, 0);
+    }
+  };
+  const int nsteps = (ke - kb + DKEYS - 1) / DKEYS;
+  issue(kb, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int row0 = 4 * q + (i >> 2);   // value row this lane points at (transposing read)
+  const int colb = (i & 3) * 8;
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
+    const int j0 = kb + sidx * DKEYS;
+    if (sidx + 1 < nsteps) issue(j0 + DKEYS, (sidx + 1) & 1);
+    if (j0 <= pmax_wave) {
+      const char* kt = kbuf0 + (sidx & 1) * TB;
+      const char* vt = vbuf0 + (sidx & 1) * TB;
+      f32x4 sacc[2][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bf16x8 ka[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          ka[t] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + kt_swz<HD>(u * 16 + i, q * (CPR / 4) + t)));
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc = mfma16(ka[t], qb[cc][t], acc);
+          sacc[cc][u] = acc;
+        }
+      }
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        float sv[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int j = j0 + u * 16 + 4 * q + rr;
+            sv[u * 4 + rr] = (j <= prow[cc] && j < ke) ? sacc[cc][u][rr] * a.scale_log2 : -INFINITY;
+          }
+        float mt = sv[0];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) mt = fmaxf(mt, sv[x]);
+        mt = max_xor16(mt);
+        mt = max_xor32(mt);
+        const float mnew = fmaxf(st[cc].m, mt);
+        float alpha = 1.f;
+        float pv[16];
+        if (mnew == -INFINITY) {
+#pragma unroll
+          for (int x = 0; x < 16; ++x) pv[x] = 0.f;
+        } else {
+          alpha = exp2_fast(st[cc].m - mnew);
+#pragma unroll
+          for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(sv[x] - mnew);
+        }
+        float ps = 0.f;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) ps += pv[x];
+        st[cc].l = st[cc].l * alpha + ps;
+        st[cc].m = mnew;
+        pb[cc][0] = pack8(pv);
+        pb[cc][1] = pack8(pv + 8);
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) st[cc].o[dt][rr] *= alpha;
+      }
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt) {
+          const uint2 lo = lds_tr(vt, vt_swz<HD>(32 * v + row0, dt * 32 + colb));
+          const uint2 hi = lds_tr(vt, vt_swz<HD>(32 * v + 16 + row0, dt * 32 + colb));
+          uint4 u4;
+          u4.x = lo.x; u4.y = lo.y; u4.z = hi.x; u4.w = hi.y;
+          const bf16x8 va = as_bf16x8(u4);
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) st[cc].o[dt] = mfma16(va, pb[cc][v], st[cc].o[dt]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next step have landed
+    __syncthreads();
+  }
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    float l = sum_xor32(sum_xor16(st[cc].l));
+    if (rvalid[cc]) {
+      const int r = rbase + w * 32 + cc * 16 + i;
+      emit_col<HD>(a, st[cc], l, b, r, h, c, prow[cc] / a.RC + 1);
+    }
+  }
+}
+
+// Sparse query block of a slice: up to kQB chunk rows; wave w takes rows
+// w, w + 4, ...  For each row and each chunk of up to 16 sparse heads of the
+// group (the MFMA columns), the row's entries of this range are staged in the
+// wave's LDS (up to kSeg at a time, one round of loads), then consumed 32 per
+// step through the wave's LDS key and value tiles (see the pipeline below).
+template <int HD>
+__device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, char* smem) {
+  constexpr int T = HD / 32;
+  constexpr int CPR = HD / 8;
+  constexpr int RPI = 64 / CPR;             // rows per wave load (16 B per lane)
+  constexpr int TB = 32 * HD * 2;           // bytes of one 32-row tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 4, i = lane & 15;
+  const int G = a.Hq / a.Hkv;
+  char* ktile = smem + w * 2 * (32 * 256);
+  char* vtile = ktile + TB;
+  int* wl = reinterpret_cast<int*>(smem + 4 * 2 * 32 * 256) + w * kSeg;
+  const size_t rstride = (size_t)a.Hkv * HD;
+  const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
+  const int kb = c * a.RC;
+  const int r1 = min(a.R, r0 + kQB);
+  const int nhc = (G + 15) / 16;
+  for (int r = r0 + w; r < r1; r += 4) {
+    const int n = a.n0 + r, p = a.L - a.N + n;
+    const int ke = min(kb + a.RC, p + 1);
+    const int nr = p / a.RC + 1;
+    const int32_t* orow = a.off + ((size_t)b * a.R + r) * (a.NC + 1);
+    const int lo = min(max(orow[c], 0), a.K);
+    const int hi = min(max(orow[c + 1], lo), a.K);
+    const int32_t* irow = a.topk + ((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.K;
+    for (int hc = 0; hc < nhc; ++hc) {
+      int myh = -1, cnt = 0;
+      for (int x = hc * 16; x < min(G, hc * 16 + 16); ++x) {
+        const int h = g * G + x;
+        if (head_sparse(a, b, h)) {
+          if (cnt == i) myh = h;
+          ++cnt;
+        }
+      }
+      if (cnt == 0) continue;
+      bf16x8 qb[T];
+      {
+        const bf16_bits* qr = a.q + (((size_t)b * a.N + n) * a.Hq + (myh < 0 ? 0 : myh)) * HD;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          uint4 u = (myh >= 0) ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
+                               : make_uint4(0, 0, 0, 0);
+          qb[t] = as_bf16x8(u);
+        }
+      }
+      ColState<HD> st;
+      st.m = -INFINITY;
+      st.l = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = lo; s0 < hi; s0 += kSeg) {
+        const int sn = min(kSeg, hi - s0);
+        // stage this part of the segment, each entry checked against the range
+        // and the row (entries past the segment read as -1)
+        int jv[kSeg / 64];
+#pragma unroll
+        for (int x = 0; x < kSeg / 64; ++x) {
+          const int e = x * 64 + lane;
+          jv[x] = (e < sn) ? irow[s0 + e] : -1;
+        }
+#pragma unroll
+        for (int x = 0; x < kSeg / 64; ++x) {
+          int j = jv[x];
+          if (j < kb || j >= ke) j = -1;
+          wl[x * 64 + lane] = j;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        // register-staged pipeline: the 32 key and value rows of step e0 are
+        // loaded into registers (whole 256-byte rows per 16 lanes, the access
+        // pattern the L2 serves fastest) while step e0 - 32 computes, then
+        // written to the wave's LDS tiles (permuted as kt_swz / vt_swz) and
+        // read back as MFMA operands.  Entries of -1 read row 0 (masked).
+        u32x4 kr[32 / RPI], vr[32 / RPI];
+#pragma unroll
+        for (int m = 0; m < 32 / RPI; ++m) {
+          const int j = wl[m * RPI + lane / CPR];
+          const size_t jr = (size_t)(j < 0 ? 0 : j) * rstride + (lane % CPR) * 8;
+          kr[m] = *reinterpret_cast<const u32x4*>(kbase + jr);
+          vr[m] = *reinterpret_cast<const u32x4*>(vbase + jr);
+        }
+        for (int e0 = 0; e0 < sn; e0 += 32) {
+          __builtin_amdgcn_s_waitcnt(0);   // this step's rows are in registers
+#pragma unroll
+          for (int m = 0; m < 32 / RPI; ++m) {
+            const int rr = m * RPI + lane / CPR, ch = lane % CPR;
+            *reinterpret_cast<u32x4*>(ktile + kt_swz<HD>(rr, ch)) = kr[m];
+            *reinterpret_cast<u32x4*>(vtile + vt_swz<HD>(rr, ch * 16)) = vr[m];
+          }
+          bool kval[2][4];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) kval[u][rr] = wl[e0 + u * 16 + 4 * q + rr] >= 0;
+          __builtin_amdgcn_s_waitcnt(0);   // tiles written
+          __builtin_amdgcn_wave_barrier();
+          if (e0 + 32 < sn) {
+#pragma unroll
+            for (int m = 0; m < 32 / RPI; ++m) {
+              const int j = wl[e0 + 32 + m * RPI + lane / CPR];
+              const size_t jr = (size_t)(j < 0 ? 0 : j) * rstride + (lane % CPR) * 8;
+              kr[m] = *reinterpret_cast<const u32x4*>(kbase + jr);
+              vr[m] = *reinterpret_cast<const u32x4*>(vbase + jr);
+            }
+          }
+          step32_lds<HD>(ktile, vtile, qb, kval, a.scale_log2, st);
+          __builtin_amdgcn_wave_barrier();   // tile reads are consumed by the MFMAs above
+        }
+      }
+      const float l = sum_xor32(sum_xor16(st.l));
+      if (myh >= 0) emit_col<HD>(a, st, l, b, r, myh, c, nr);
+    }
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(ST, 2) void k_attn_slices(SliceArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kLds];
+  __shared__ int s_item[4];
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcd - 1);  // HW_REG_XCC_ID
+  int qx = (int)xcc, tried = 0;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int found = 0;
+      while (tried < kXcd) {
+        const int total = a.sched[kXcd + qx];
+        if (total > 0 && a.ctr[qx] < (uint32_t)total) {
+          const uint32_t t = atomicAdd(&a.ctr[qx], 1u);
+          if (t < (uint32_t)total) {
+            // the queue's slice holding item t (binary search over the prefix)
+            const int cnt = a.sched[qx];
+            const int32_t* pre = q_pre(a, qx);
+            int lo = 0, hi = cnt - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (pre[mid] <= (int)t) lo = mid;
+              else hi = mid - 1;
+            }
+            s_item[0] = q_sid(a, qx)[lo];
+            s_item[1] = (int)t - pre[lo];
+            found = 1;
+            break;
+          }
+        }
+        qx = (qx + 1) & (kXcd - 1);
+        ++tried;
+      }
+      s_item[2] = found;
+      s_item[3] = tried;
+    }
+    __syncthreads();
+    const int found = s_item[2];
+    const int s = s_item[0], it = s_item[1];
+    tried = s_item[3];
+    qx = (int)((xcc + tried) & (kXcd - 1));
+    __syncthreads();
+    if (!found) return;
+    const int c = s % a.NC, bg = s / a.NC;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const SliceItems S = slice_items(a, b, g, c);
+    // dense items spread evenly through the slice's item sequence
+    const int tot = S.n_dense + S.n_sparse;
+    const long long dk0 = (long long)it * S.n_dense / tot;
+    const long long dk1 = (long long)(it + 1) * S.n_dense / tot;
+    if (dk1 > dk0) {
+      const int d = (int)dk0;                 // dense item index
+      const int hi = d / S.nt, tile = S.r_c / DROWS + d % S.nt;
+      // the hi-th dense head of the group
+      const int G = a.Hq / a.Hkv;
+      int h = -1, k = 0;
+      for (int x = 0; x < G; ++x)
+        if (!head_sparse(a, b, g * G + x) && k++ == hi) {
+          h = g * G + x;
+          break;
+        }
+      dense_tile<HD>(a, b, h, tile, c, smem);
+    } else {
+      const int sp = it - (int)dk1;           // sparse item index
+      sparse_block<HD>(a, b, g, c, S.r_c + sp * kQB, smem);
+    }
+    __syncthreads();
+  }
+}
+
+// Merge of the per-range partials of rows that see more than one range: one
+// workgroup per (sequence, row); thread t takes head t / 8 (in rounds of 32
+// heads), dims 16 * (t % 8) .. + 16.
+template <int HD>
+__global__ __launch_bounds__(ST) void k_merge_ranges(SliceArgs a) {
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int n = a.n0 + r, p = a.L - a.N + n;
+  const int nr = p / a.RC + 1;
+  if (nr == 1) return;
+  constexpr int TPH = HD / 16;            // threads per head
+  constexpr int HPR = ST / TPH;           // heads per round
+  const int hl = threadIdx.x / TPH, d0 = (threadIdx.x % TPH) * 16;
+  for (int h0 = 0; h0 < a.Hq; h0 += HPR) {
+    const int h = h0 + hl;
+    if (h >= a.Hq) break;
+    float m = -INFINITY;
+    for (int c = 0; c < nr; ++c)
+      m = fmaxf(m, a.part_lse[(((size_t)b * a.R + r) * a.NC + c) * a.Hq + h]);
+    float acc[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) acc[x] = 0.f;
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+      for (int c = 0; c < nr; ++c) {
+        const size_t slot = (((size_t)b * a.R + r) * a.NC + c) * a.Hq + h;
+        const float lse = a.part_lse[slot];
+        if (lse == -INFINITY) continue;
+        const float wgt = exp2_fast(lse - m);
+        wsum += wgt;
+        const float4* src = reinterpret_cast<const float4*>(a.part_o + slot * HD + d0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float4 v = src[x];
+          acc[4 * x] = fmaf(wgt, v.x, acc[4 * x]);
+          acc[4 * x + 1] = fmaf(wgt, v.y, acc[4 * x + 1]);
+          acc[4 * x + 2] = fmaf(wgt, v.z, acc[4 * x + 2]);
+          acc[4 * x + 3] = fmaf(wgt, v.w, acc[4 * x + 3]);
+        }
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const size_t orow = ((size_t)b * a.N + n) * a.Hq + h;
+    const float gt = a.gate ? a.gate[orow] : 1.f;
+    float4* dst = reinterpret_cast<float4*>(a.out + orow * HD + d0);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      float o[4];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        float val = acc[4 * x + y] * inv;
+        if (a.gate) val = fmaf(gt, val, (1.f - gt) * a.y2[orow * HD + d0 + 4 * x + y]);
+        o[y] = val;
+      }
+      dst[x] = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+int g_grid_cache[64][2];
+
+}  // namespace
+
+SlicePlan slice_plan(const Dims& D, int R) {
+  SlicePlan P;
+  P.RC = kSliceKeys;
+  const int p_last = D.L - 1;   // bound for any chunk
+  P.NC = p_last / P.RC + 1;
+  (void)R;
+  const long long nslices = (long long)D.B * D.Hkv * P.NC;
+  P.cap = (int)((nslices + kXcd - 1) / kXcd);
+  return P;
+}
+
+size_t slice_ws_bytes(const Dims& D, int R) {
+  const SlicePlan P = slice_plan(D, R);
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  size_t b = 0;
+  b += al((size_t)D.B * R * (P.NC + 1) * 4);                      // offsets
+  b += al((16 + (size_t)2 * kXcd * P.cap) * 4);                   // queue tables
+  b += al(kXcd * 4 * 16);                                         // counters
+  b += al((size_t)D.B * R * P.NC * D.Hq * D.d * 4);               // partial outputs
+  b += al((size_t)D.B * R * P.NC * D.Hq * 4);                     // partial lse
+  return b;
+}
+
+bool slice_attention_supported(const Dims& D) {
+  return D.qkv_bf16 && (D.d == 64 || D.d == 128) && D.L <= 256 * kSliceKeys;
+}
+
+hipError_t launch_attention_slices(const Dims& D, const AttnArgs& aa, void* ws, hipStream_t s) {
+  if (D.B == 0 || aa.R == 0) return hipSuccess;
+  const SlicePlan P = slice_plan(D, aa.R);
+  SliceArgs a{};
+  a.q = (const bf16_bits*)aa.q; a.k = (const bf16_bits*)aa.k; a.v = (const bf16_bits*)aa.v;
+  a.topk = aa.topk; a.idx_rows_per_b = aa.idx_rows_per_b; a.idx_n_base = aa.idx_n_base;
+  a.gate = aa.gate; a.y2 = aa.y2; a.route = aa.route; a.out = aa.out;
+  a.B = D.B; a.N = D.N; a.L = D.L; a.Hq = D.Hq; a.Hkv = D.Hkv; a.K = D.K;
+  a.n0 = aa.n0; a.R = aa.R;
+  a.RC = P.RC;
+  // ranges seen by the chunk's last row bound the partial slots
+  a.NC = (D.L - D.N + aa.n0 + aa.R - 1) / P.RC + 1;
+  a.cap = P.cap;
+  a.scale_log2 = D.scale * kLog2e;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  char* w = (char*)ws;
+  size_t o = 0;
+  a.off = (const int32_t*)(w + o);   o += al((size_t)D.B * aa.R * (P.NC + 1) * 4);
+  int32_t* sched = (int32_t*)(w + o); o += al((16 + (size_t)2 * kXcd * P.cap) * 4);
+  a.sched = sched;
+  a.ctr = (uint32_t*)(w + o);        o += al(kXcd * 4 * 16);
+  a.part_o = (float*)(w + o);        o += al((size_t)D.B * aa.R * P.NC * D.Hq * D.d * 4);
+  a.part_lse = (float*)(w + o);
+  const long long rows = (long long)D.B * aa.R;
+  {
+    ProfScope ps(s, kStagePrep);
+    hipLaunchKernelGGL(k_range_offsets, dim3((unsigned)((rows + 3) / 4)), dim3(ST), 0, s, a);
+    hipLaunchKernelGGL(k_sched, dim3(1), dim3(ST), 0, s, a, sched);
+  }
+  // persistent grid: what the device holds at once
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int& grid = g_grid_cache[dev & 63][D.d == 128 ? 1 : 0];
+  if (grid == 0) {
+    int cus = 0, per = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = D.d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_attn_slices<128>, ST, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_attn_slices<64>, ST, 0);
+    if (e != hipSuccess) return e;
+    grid = cus * std::max(1, per);
+  }
+  {
+    ProfScope ps(s, kStageAttention);
+    if (D.d == 128) hipLaunchKernelGGL(k_attn_slices<128>, dim3(grid), dim3(ST), 0, s, a);
+    else hipLaunchKernelGGL(k_attn_slices<64>, dim3(grid), dim3(ST), 0, s, a);
+  }
+  {
+    ProfScope ps(s, kStageMerge);
+    if (D.d == 128) hipLaunchKernelGGL(k_merge_ranges<128>, dim3(aa.R, D.B), dim3(ST), 0, s, a);
+    else hipLaunchKernelGGL(k_merge_ranges<64>, dim3(aa.R, D.B), dim3(ST), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

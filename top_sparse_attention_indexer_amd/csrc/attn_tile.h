@@ -1,0 +1,171 @@
+// Per-step core of the bf16 MFMA attention kernels (gfx950), shared by the
+// prefill kernels: one wave, 32 keys per step, the 16 MFMA columns being
+// query heads or query rows.
+//
+//   S^T [16 keys x 16 cols] = K_tile [16 x d] . Q^T [d x 16]   (two halves)
+//   online softmax per column, in registers (a lane owns one column; the
+//     four lane quads hold 4 keys each of every 16-key half);
+//   O^T [16 dims x 16 cols] += V^T [16 dims x 32 keys] . P^T [32 keys x 16]
+//     with P^T the MFMA B operand straight from registers and V^T read from a
+//     row-major LDS tile with the transposing LDS load.
+// Scores are kept in the log2 domain (scale * log2(e) folded in), so the
+// exponentials are single v_exp_f32 instructions.
+#pragma once
+
+#include "common.h"
+#include "mfma.h"
+
+namespace dsa {
+
+constexpr int VSTR = 288;        // LDS row stride of a 32 x d value tile (bytes)
+constexpr int KSTR = 272;        // LDS row stride of a key tile (bytes)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Shared per-step core: given this wave's two 16-key halves (A operands for
+// S^T already loaded), the 32 x d value tile in LDS, update the running
+// state of the lane's column.
+template <int HD>
+struct ColState {
+  float m, l;
+  f32x4 o[HD / 16];
+};
+
+template <int HD>
+__device__ __forceinline__ void step_core(const uint4 (&ka)[2][HD / 32], const bf16x8 (&qb)[HD / 32],
+                                          const bool (&kvalid)[2][4], const char* vtile,
+                                          float scale_log2, ColState<HD>& st) {
+  constexpr int T = HD / 32;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, i = lane & 15;
+  float s[8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[u][t]), qb[t], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[u * 4 + r] = kvalid[u][r] ? acc[r] * scale_log2 : -INFINITY;
+  }
+  float mt = s[0];
+#pragma unroll
+  for (int x = 1; x < 8; ++x) mt = fmaxf(mt, s[x]);
+  mt = max_xor16(mt);
+  mt = max_xor32(mt);
+  const float mnew = fmaxf(st.m, mt);
+  float alpha = 1.f;
+  float p[8];
+  if (mnew == -INFINITY) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) p[x] = 0.f;
+  } else {
+    alpha = exp2_fast(st.m - mnew);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) p[x] = exp2_fast(s[x] - mnew);
+  }
+  float ps = 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) ps += p[x];
+  st.l = st.l * alpha + ps;  // this lane's keys only; summed over quads at the end
+  st.m = mnew;
+  const bf16x8 pb = pack8(p);
+  // value tile rows: first half keys 4q+k, second half 16+4q+k; this lane
+  // (4k + c within its 16-lane group) points at row 4q + i/4, dims 4*(i%4)
+  const int row0 = 4 * q + (i >> 2);
+  const int colb = (i & 3) * 8;  // bytes
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) {
+    const uint2 lo = lds_tr(vtile, row0 * VSTR + dt * 32 + colb);
+    const uint2 hi = lds_tr(vtile, (16 + row0) * VSTR + dt * 32 + colb);
+    uint4 u;
+    u.x = lo.x; u.y = lo.y; u.z = hi.x; u.w = hi.y;
+    f32x4 o = st.o[dt];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] *= alpha;
+    st.o[dt] = mfma16(as_bf16x8(u), pb, o);
+  }
+}
+
+// Byte offset of bytes [cb, cb + 8) of row R in a value tile of HD-wide bf16
+// rows stored back to back (row stride HD * 2 bytes, as the direct
+// global-to-LDS load writes them) with the 16-byte chunks of row R permuted
+// by chunk ^ 2 * (R mod CPR/2): the transposing read of four consecutive rows
+// (one 16-lane group) then touches four different bank ranges.
+template <int HD>
+__device__ __forceinline__ int vt_swz(int R, int cb) {
+  constexpr int CPR = HD / 8;
+  const int c16 = cb >> 4;
+  return R * (HD * 2) + ((c16 ^ ((R & (CPR / 2 - 1)) << 1)) << 4) + (cb & 15);
+}
+
+// Byte offset of 16-byte chunk c16 of row R in a key tile of HD-wide bf16
+// rows stored back to back, chunks permuted by c16 ^ (R mod CPR): sixteen
+// lanes reading the same chunk of sixteen consecutive rows hit sixteen
+// different bank ranges.
+template <int HD>
+__device__ __forceinline__ int kt_swz(int R, int c16) {
+  constexpr int CPR = HD / 8;
+  return R * (HD * 2) + ((c16 ^ (R & (CPR - 1))) << 4);
+}
+
+// 32-key step with both tiles in LDS (rows back to back, permuted as in
+// kt_swz / vt_swz): the key rows are read as the A operand (lane quad q
+// takes bytes 64 t + 16 q of its key row, the order the query operand uses),
+// the value rows with the transposing read.
+template <int HD>
+__device__ __forceinline__ void step32_lds(const char* ktile, const char* vtile,
+                                           const bf16x8 (&qb)[HD / 32], const bool (&kvalid)[2][4],
+                                           float scale_log2, ColState<HD>& st) {
+  constexpr int T = HD / 32;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, i = lane & 15;
+  float s[8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    uint4 ka[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      ka[t] = *reinterpret_cast<const uint4*>(ktile + kt_swz<HD>(u * 16 + i, 4 * t + q));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[t]), qb[t], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[u * 4 + r] = kvalid[u][r] ? acc[r] * scale_log2 : -INFINITY;
+  }
+  float mt = s[0];
+#pragma unroll
+  for (int x = 1; x < 8; ++x) mt = fmaxf(mt, s[x]);
+  mt = max_xor16(mt);
+  mt = max_xor32(mt);
+  const float mnew = fmaxf(st.m, mt);
+  float alpha = 1.f;
+  float p[8];
+  if (mnew == -INFINITY) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) p[x] = 0.f;
+  } else {
+    alpha = exp2_fast(st.m - mnew);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) p[x] = exp2_fast(s[x] - mnew);
+  }
+  float ps = 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) ps += p[x];
+  st.l = st.l * alpha + ps;
+  st.m = mnew;
+  const bf16x8 pb = pack8(p);
+  const int row0 = 4 * q + (i >> 2);
+  const int colb = (i & 3) * 8;
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) {
+    const uint2 lo = lds_tr(vtile, vt_swz<HD>(row0, dt * 32 + colb));
+    const uint2 hi = lds_tr(vtile, vt_swz<HD>(16 + row0, dt * 32 + colb));
+    uint4 u;
+    u.x = lo.x; u.y = lo.y; u.z = hi.x; u.w = hi.y;
+    f32x4 o = st.o[dt];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] *= alpha;
+    st.o[dt] = mfma16(as_bf16x8(u), pb, o);
+  }
+}
+
+}  // namespace dsa

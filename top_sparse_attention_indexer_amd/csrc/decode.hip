@@ -1853,7 +1853,10 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   record_launch(ws, a.epoch);
   void* args[] = {&a};
   // the completion event rides on the kernel's own dispatch
-  e = hipExtLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s, nullptr, so.done, 0);
+  {
+    ProfScope ps(s, kStageDecode);
+    e = hipExtLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s, nullptr, so.done, 0);
+  }
   so.last = s;
   so.have_last = true;
   return e;

@@ -93,6 +93,9 @@ struct Plan {
   size_t idx_off = 0, idx_bytes = 0;    // internal index rows of one chunk
   size_t part_off = 0, part_bytes = 0;  // attention partials of one chunk
   int splits_sparse = 1, splits_dense = 1;
+  bool slices = false;  // key-range blocked MFMA attention (prefill, bf16)
+  int Ra = 0;           // query rows per attention launch on that path
+  size_t sl_off = 0, sl_bytes = 0;
   size_t total = 0;
 };
 
@@ -116,6 +119,19 @@ int prefill_chunk_rows(const dsa::Dims& D) {
   return (int)std::min<size_t>(r, (size_t)D.N);
 }
 
+// Budget of per-range attention partials per launch of the key-range path;
+// rows per launch are a multiple of 1024 (or all rows).
+constexpr size_t kPartialBudget = size_t(6) << 30;
+int slice_chunk_rows(const dsa::Dims& D) {
+  const size_t per_row = dsa::slice_ws_bytes(D, 1);
+  size_t r = std::max<size_t>(1024, kPartialBudget / std::max<size_t>(per_row, 1)) / 1024 * 1024;
+  return (int)std::min<size_t>(r, (size_t)D.N);
+}
+
+bool use_slices(const dsa::Dims& D) {
+  return D.N > kDecodeRows && dsa::slice_attention_supported(D);
+}
+
 Plan plan_topk(const dsa::Dims& D) {
   Plan P;
   P.decode = D.N <= kDecodeRows;
@@ -129,6 +145,13 @@ Plan plan_attn(const dsa::Dims& D) {
   Plan P;
   P.decode = D.N <= kDecodeRows;
   P.R = D.N;
+  if (use_slices(D)) {
+    P.slices = true;
+    P.Ra = slice_chunk_rows(D);
+    P.sl_bytes = dsa::slice_ws_bytes(D, P.Ra);
+    P.total = align256(P.sl_bytes);
+    return P;
+  }
   dsa::attn_pick_splits(D, D.N, P.splits_sparse, P.splits_dense);
   P.part_bytes = dsa::attn_part_bytes(D, D.N, std::max(P.splits_sparse, P.splits_dense));
   P.total = align256(P.part_bytes);
@@ -159,7 +182,9 @@ Plan plan_fused(const dsa::Dims& D, bool allow_single_launch = true) {
   Plan P;
   if (allow_single_launch && plan_fused_decode(D, P)) return P;
   P.decode = D.N <= kDecodeRows;
-  P.R = P.decode ? D.N : prefill_chunk_rows(D);
+  P.slices = use_slices(D);
+  P.Ra = P.slices ? slice_chunk_rows(D) : D.N;
+  P.R = P.decode ? D.N : std::min(P.Ra, prefill_chunk_rows(D));
   P.ld = (size_t)D.L;
   size_t off = 0;
   P.scores_off = off;
@@ -171,12 +196,18 @@ Plan plan_fused(const dsa::Dims& D, bool allow_single_launch = true) {
     off = align256(off + P.tk_bytes);
   }
   P.idx_off = off;
-  P.idx_bytes = (size_t)D.B * P.R * D.K * sizeof(int32_t);
+  P.idx_bytes = (size_t)D.B * (P.slices ? P.Ra : P.R) * D.K * sizeof(int32_t);
   off = align256(off + P.idx_bytes);
-  dsa::attn_pick_splits(D, P.R, P.splits_sparse, P.splits_dense);
-  P.part_off = off;
-  P.part_bytes = dsa::attn_part_bytes(D, P.R, std::max(P.splits_sparse, P.splits_dense));
-  off = align256(off + P.part_bytes);
+  if (P.slices) {
+    P.sl_off = off;
+    P.sl_bytes = dsa::slice_ws_bytes(D, P.Ra);
+    off = align256(off + P.sl_bytes);
+  } else {
+    dsa::attn_pick_splits(D, P.R, P.splits_sparse, P.splits_dense);
+    P.part_off = off;
+    P.part_bytes = dsa::attn_part_bytes(D, P.R, std::max(P.splits_sparse, P.splits_dense));
+    off = align256(off + P.part_bytes);
+  }
   P.total = off;
   return P;
 }
@@ -284,6 +315,18 @@ dsa_status dsa_sparse_attn(const dsa_problem* p, const void* q, const void* k, c
   if ((st = check_gate(gate, y2)) != DSA_OK) return st;
   const Plan P = plan_attn(D);
   if ((st = check_ws(P, ws, ws_bytes)) != DSA_OK) return st;
+  if (P.slices) {
+    hipError_t e = hipSuccess;
+    for (int n0 = 0; n0 < D.N && e == hipSuccess; n0 += P.Ra) {
+      dsa::AttnArgs a{};
+      a.q = q; a.k = k; a.v = v;
+      a.topk = topk_idx; a.idx_rows_per_b = D.N; a.idx_n_base = 0;
+      a.gate = gate; a.y2 = y2; a.route = route; a.out = out;
+      a.n0 = n0; a.R = std::min(P.Ra, D.N - n0);
+      e = dsa::launch_attention_slices(D, a, (char*)ws + P.sl_off, (hipStream_t)stream);
+    }
+    return hip_status(e, "dsa_sparse_attn");
+  }
   dsa::AttnArgs a{};
   a.q = q; a.k = k; a.v = v;
   a.topk = topk_idx; a.idx_rows_per_b = D.N; a.idx_n_base = 0;
@@ -330,20 +373,33 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
   dsa::forget_launch(ws);
   float* scores = (float*)(w + P.scores_off);
   int32_t* idx_chunk = (int32_t*)(w + P.idx_off);
-  float* part = P.part_bytes ? (float*)(w + P.part_off) : nullptr;
   hipError_t e = hipSuccess;
-  const bool mfma = !P.decode && dsa::mfma_attention_supported(D);
-  if (mfma && route && P.R < D.N) {
-    // dense-route heads need no indices: one launch over every query row
-    // (row chunks exist only for the score buffer of the sparse heads)
-    dsa::AttnArgs a{};
-    a.q = q; a.k = k; a.v = v;
-    a.topk = idx_chunk; a.idx_rows_per_b = P.R; a.idx_n_base = 0;
-    a.gate = gate; a.y2 = y2; a.route = route; a.out = out;
-    a.n0 = 0; a.R = D.N;
-    a.skip_sparse = true;
-    e = dsa::launch_attention_mfma(D, a, s);
+  if (P.slices) {
+    // all index rows of an attention launch first (indexer and top-k per
+    // chunk of score rows), then one launch for both routes over them
+    for (int na = 0; na < D.N && e == hipSuccess; na += P.Ra) {
+      const int Rc = std::min(P.Ra, D.N - na);
+      int32_t* idx = topk_idx_out ? topk_idx_out : idx_chunk;
+      const int rows_per_b = topk_idx_out ? D.N : P.Ra;
+      const int n_base = topk_idx_out ? 0 : na;
+      for (int n0 = na; n0 < na + Rc && e == hipSuccess; n0 += P.R) {
+        const int R = std::min(P.R, na + Rc - n0);
+        const int ncols = D.L - D.N + n0 + R;  // keys visible to the last row of the chunk
+        e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
+        if (e == hipSuccess)
+          e = dsa::launch_topk_rows(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route, s);
+      }
+      if (e != hipSuccess) break;
+      dsa::AttnArgs a{};
+      a.q = q; a.k = k; a.v = v;
+      a.topk = idx; a.idx_rows_per_b = rows_per_b; a.idx_n_base = n_base;
+      a.gate = gate; a.y2 = y2; a.route = route; a.out = out;
+      a.n0 = na; a.R = Rc;
+      e = dsa::launch_attention_slices(D, a, w + P.sl_off, s);
+    }
+    return hip_status(e, "dsa_fused_forward");
   }
+  float* part = P.part_bytes ? (float*)(w + P.part_off) : nullptr;
   for (int n0 = 0; n0 < D.N && e == hipSuccess; n0 += P.R) {
     const int R = std::min(P.R, D.N - n0);
     const int ncols = D.L - D.N + n0 + R;  // keys visible to the last row of the chunk
@@ -368,8 +424,7 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
     a.n0 = n0; a.R = R;
     a.splits_sparse = P.splits_sparse;
     a.splits_dense = P.splits_dense;
-    if (mfma) {
-      a.skip_dense = route && P.R < D.N;   // already done above
+    if (!P.decode && dsa::mfma_attention_supported(D)) {
       a.sparse_heads_per_item = sparse_heads_per_item(D);
       e = dsa::launch_attention_mfma(D, a, s);
     } else {
@@ -392,6 +447,20 @@ dsa_status dsa_exec_status(const void* ws, void* stream) {
 }
 
 void dsa_set_wait_limit(uint32_t polls) { dsa::set_wait_limit(polls); }
+
+dsa_status dsa_profile_start(int32_t max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(DSA_ERR_INVALID_ARG, "max_launches %d not in [1, 2^20]", max_launches);
+  return hip_status(dsa::prof_start(max_launches), "dsa_profile_start");
+}
+
+dsa_status dsa_profile_stop(double* ms, int32_t* launches, int32_t n_stages, int64_t* dropped) {
+  if (n_stages < 0) return fail(DSA_ERR_INVALID_ARG, "n_stages is negative");
+  long long d = 0;
+  const hipError_t e = dsa::prof_stop(ms, launches, n_stages, &d);
+  if (dropped) *dropped = d;
+  return hip_status(e, "dsa_profile_stop");
+}
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
 

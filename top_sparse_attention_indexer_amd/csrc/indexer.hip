@@ -224,6 +224,7 @@ hipError_t launch_indexer_tiles(const Dims& D, const void* q_idx, const void* k_
                                 int ncols, float* out, size_t ld, bool write_masked,
                                 const uint8_t* route, hipStream_t s) {
   if (D.B == 0 || R == 0 || ncols == 0) return hipSuccess;
+  ProfScope ps(s, kStageIndexer);
   if (D.idx_bf16 && (D.didx == 32 || D.didx == 64 || D.didx == 128)) {
     const dim3 g((ncols + 127) / 128, (R + 63) / 64, D.B);
 #define DSA_IDX_MFMA(DI)                                                                       \
@@ -253,6 +254,7 @@ hipError_t launch_indexer_scan(const Dims& D, const void* q_idx, const void* k_i
                                const uint8_t* route, hipStream_t s) {
   if (D.B == 0 || R == 0 || ncols == 0) return hipSuccess;
   if (R > 8) return hipErrorInvalidValue;
+  ProfScope ps(s, kStageIndexer);
   if (D.idx_bf16)
     return scan_dispatch(D, (const bf16_bits*)q_idx, (const bf16_bits*)k_idx, n0, R, ncols, out, ld,
                          write_masked, route, s);

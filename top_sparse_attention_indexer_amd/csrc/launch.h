@@ -116,6 +116,20 @@ void set_wait_limit(uint32_t polls);
 int decode_exec_status(const void* ws, hipStream_t s, hipError_t* err);
 void forget_launch(const void* ws);
 
+// ---- stage timing (dsa_profile_start / dsa_profile_stop) -----------------------
+enum Stage { kStageIndexer = 0, kStageTopk = 1, kStageAttention = 2, kStageMerge = 3,
+             kStageDecode = 4, kStagePrep = 5, kStages = 6 };
+void prof_begin(hipStream_t s, int stage);
+void prof_end(hipStream_t s);
+hipError_t prof_start(int max_launches);
+hipError_t prof_stop(double* ms, int32_t* launches, int n_stages, long long* dropped);
+// Marks the launches enqueued during its lifetime as one timed launch of `stage`.
+struct ProfScope {
+  hipStream_t s;
+  ProfScope(hipStream_t s_, int stage) : s(s_) { prof_begin(s, stage); }
+  ~ProfScope() { prof_end(s); }
+};
+
 // ---- misc ------------------------------------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s);
 

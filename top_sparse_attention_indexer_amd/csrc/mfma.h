@@ -17,6 +17,9 @@ namespace dsa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// 16 raw bytes as a native vector (HIP's uint4 is a struct whose copies can
+// keep arrays of it out of registers)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 

@@ -496,6 +496,7 @@ hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n
   // list in LDS); longer rows: the multi-pass kernel
   const long long vmax = (long long)D.L - D.N + n0 + R;
   const dim3 grid(R, D.B);
+  ProfScope ps(s, kStageTopk);
   if (vmax <= 32768)
     hipLaunchKernelGGL((k_topk_cand<512, 6144>), grid, dim3(512), 0, s, scores, ld, D.N, D.L, D.K,
                        n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq);
@@ -524,6 +525,7 @@ hipError_t launch_topk_split(const Dims& D, const float* scores, size_t ld, int 
   ws.hist = (uint32_t*)wsp;
   ws.cnt = ws.hist + (size_t)rows * kHistWords;
   ws.state = ws.cnt + (size_t)rows * ws.nchunks * 2;
+  ProfScope ps(s, kStageTopk);
   hipError_t e = launch_fill_u32(ws.hist, (size_t)rows * kHistWords, 0u, s);
   if (e != hipSuccess) return e;
   const dim3 grid(ws.nchunks, rows);
