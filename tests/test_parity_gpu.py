@@ -217,6 +217,38 @@ def test_shared_key_indexer(N, L, announce):
     check_rows(w, x, out, idx, rows=rows, use_route=False)
 
 
+@pytest.mark.parametrize("kind", ["sampled_keys_high", "all_equal"])
+def test_prefill_selection_fallback(kind, announce):
+    """Prefill rows whose candidate list cannot be used must take the exact
+    streamed selection.  sampled_keys_high: only every 4th key (the keys a
+    strided sample of an 8192-key row sees) has a nonzero score, so the
+    threshold estimated from the sample lets through fewer than K keys;
+    all_equal: every score is equal, so every key is a candidate and the list
+    overflows; the K lowest positions win."""
+    w = _w(1, 64, 8192, 8, 2, 128, 64, 2048, seed=41)
+    x = synth.make_inputs(w)
+    if kind == "sampled_keys_high":
+        x["q_idx"][:] = 1.0
+        rng = np.random.default_rng(5)
+        k = np.zeros_like(x["k_idx"])
+        k[:, ::4, :] = rng.integers(0, 9, size=k[:, ::4, :].shape)
+        k[:, ::4, 0] = np.maximum(k[:, ::4, 0], 1)      # every sampled key scores >= 1
+        x["k_idx"] = k.astype(np.float32)
+    else:
+        x["q_idx"][:] = 1.0
+        x["k_idx"][:] = 1.0
+    announce(f"fused_forward prefill fallback {kind} {w}")
+    out, idx = run_fused(w, x)
+    check_index_structure(w, idx)
+    if kind == "all_equal":
+        assert torch.equal(idx[0, :, :].cpu(),
+                           torch.arange(w.top_k, dtype=torch.int32).expand(w.n_q, -1))
+    else:
+        # the last rows see 2048 nonzero keys: exactly those are selected
+        assert torch.all(idx[0, 60:] % 4 == 0).item()
+    check_rows(w, x, out, idx, rows=[0, 1, 31, 62, 63])
+
+
 def test_all_dense_route_skips_indexer(announce):
     w = _w(2, 50, 200, 4, 2, 128, 64, 16)
     x = synth.make_inputs(w)

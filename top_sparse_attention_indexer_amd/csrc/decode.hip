@@ -237,13 +237,18 @@ __device__ __forceinline__ bool rows_ready(const DecodeArgs& a, int b, int* flag
 // the sequence cannot pass the wait it gave up at, so no valid result of the
 // sequence is written after these.
 template <int HD>
-__device__ void abandon(const DecodeArgs& a, int b) {
-  const size_t n_out = (size_t)a.N * a.Hq * HD;
-  float* o = a.out + (size_t)b * n_out;
+__device__ __attribute__((noinline)) void abandon_rows(float* out, int32_t* list, int N, int Hq,
+                                                      int K, int b) {
+  const size_t n_out = (size_t)N * Hq * HD;
+  float* o = out + (size_t)b * n_out;
   const float qnan = __uint_as_float(0x7fc00000u);
   for (size_t i = threadIdx.x; i < n_out; i += DT) o[i] = qnan;
-  int32_t* l = a.list + (size_t)b * a.N * a.K;
-  for (size_t i = threadIdx.x; i < (size_t)a.N * a.K; i += DT) l[i] = -1;
+  int32_t* l = list + (size_t)b * N * K;
+  for (size_t i = threadIdx.x; i < (size_t)N * K; i += DT) l[i] = -1;
+}
+template <int HD>
+__device__ __forceinline__ void abandon(const DecodeArgs& a, int b) {
+  abandon_rows<HD>(a.out, a.list, a.N, a.Hq, a.K, b);
 }
 
 // kk-th largest (from the top) over hist[0..nb): bin and count above it.
@@ -1467,15 +1472,8 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       const uint64_t* fs = a.fstat + (size_t)row * nst * 2;
       uint32_t kmax = 0, kmin = 0xffffffffu;
       uint64_t emax = 0;
-      uint64_t sw[8][2];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int i = min((int)threadIdx.x + q * DT, nst - 1);
-        sw[q][0] = ld_dev64(fs + 2 * i);
-        sw[q][1] = ld_dev64(fs + 2 * i + 1);
-      }
       uint64_t v16[16];
-      auto load16 = [&](int i0) {
+      auto load16 = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int i = i0 + x * DT + (int)threadIdx.x;
@@ -1485,13 +1483,24 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       };
       load16(0);
+      // the records, four per thread and round (one round for up to 256
+      // chunks), reduced while the candidates are in flight
+      for (int q0 = 0; q0 * DT < nst; q0 += 4) {
+        uint64_t sw[4][2];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if ((int)threadIdx.x + q * DT < nst) {
-          kmax = max(kmax, (uint32_t)sw[q][0]);
-          kmin = min(kmin, (uint32_t)(sw[q][0] >> 32));
-          emax = max(emax, sw[q][1]);
+        for (int q = 0; q < 4; ++q) {
+          const int i = min((int)threadIdx.x + (q0 + q) * DT, nst - 1);
+          sw[q][0] = ld_dev64(fs + 2 * i);
+          sw[q][1] = ld_dev64(fs + 2 * i + 1);
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if ((int)threadIdx.x + (q0 + q) * DT < nst) {
+            kmax = max(kmax, (uint32_t)sw[q][0]);
+            kmin = min(kmin, (uint32_t)(sw[q][0] >> 32));
+            emax = max(emax, sw[q][1]);
+          }
+      }
       kmax = wave_max_u32(kmax);
       kmin = wave_min_u32(kmin);
       emax = wave_max_u64(emax);
@@ -1539,10 +1548,11 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
         const int per = a.Cpad / DT;
         const uint64_t* mine = cbuf + (size_t)threadIdx.x * per;
         uint32_t sel = 0;
-        ulonglong2 v2[16];
+        typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+        u64x2 v2[16];
 #pragma unroll
         for (int x = 0; x < 32; x += 2)
-          v2[x / 2] = *reinterpret_cast<const ulonglong2*>(mine + min(x, per - 2));
+          v2[x / 2] = *reinterpret_cast<const u64x2*>(mine + min(x, per - 2));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < 32; x += 2) {

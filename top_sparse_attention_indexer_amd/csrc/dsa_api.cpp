@@ -95,6 +95,9 @@ struct Plan {
   int splits_sparse = 1, splits_dense = 1;
   bool slices = false;  // key-range blocked MFMA attention (prefill, bf16)
   int Ra = 0;           // query rows per attention launch on that path
+  bool onchip = false;  // indexer + top-k without a score matrix
+  int Rs = 0;           // query rows per launch of that pair
+  size_t it_off = 0, it_bytes = 0;
   size_t sl_off = 0, sl_bytes = 0;
   size_t total = 0;
 };
@@ -119,6 +122,8 @@ int prefill_chunk_rows(const dsa::Dims& D) {
   return (int)std::min<size_t>(r, (size_t)D.N);
 }
 
+// Budget of indexer candidate lists per launch of the on-chip indexer + top-k.
+constexpr size_t kCandBudget = size_t(1) << 30;
 // Budget of per-range attention partials per launch of the key-range path;
 // rows per launch are a multiple of 1024 (or all rows).
 constexpr size_t kPartialBudget = size_t(6) << 30;
@@ -184,12 +189,22 @@ Plan plan_fused(const dsa::Dims& D, bool allow_single_launch = true) {
   P.decode = D.N <= kDecodeRows;
   P.slices = use_slices(D);
   P.Ra = P.slices ? slice_chunk_rows(D) : D.N;
+  P.onchip = P.slices && dsa::idx_topk_supported(D);
   P.R = P.decode ? D.N : std::min(P.Ra, prefill_chunk_rows(D));
   P.ld = (size_t)D.L;
   size_t off = 0;
-  P.scores_off = off;
-  P.scores_bytes = (size_t)D.B * P.R * D.L * sizeof(float);
-  off = align256(off + P.scores_bytes);
+  if (P.onchip) {
+    // candidate lists of up to kCandBudget bytes per launch
+    const size_t per_row = dsa::idx_topk_ws_bytes(D, 1);
+    P.Rs = (int)std::min<size_t>((size_t)P.Ra, std::max<size_t>(64, kCandBudget / per_row));
+    P.it_off = off;
+    P.it_bytes = dsa::idx_topk_ws_bytes(D, P.Rs);
+    off = align256(off + P.it_bytes);
+  } else {
+    P.scores_off = off;
+    P.scores_bytes = (size_t)D.B * P.R * D.L * sizeof(float);
+    off = align256(off + P.scores_bytes);
+  }
   if (P.decode) {
     P.tk_off = off;
     P.tk_bytes = dsa::split_topk_ws_bytes(D, P.R);
@@ -382,12 +397,20 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
       int32_t* idx = topk_idx_out ? topk_idx_out : idx_chunk;
       const int rows_per_b = topk_idx_out ? D.N : P.Ra;
       const int n_base = topk_idx_out ? 0 : na;
-      for (int n0 = na; n0 < na + Rc && e == hipSuccess; n0 += P.R) {
-        const int R = std::min(P.R, na + Rc - n0);
-        const int ncols = D.L - D.N + n0 + R;  // keys visible to the last row of the chunk
-        e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
-        if (e == hipSuccess)
-          e = dsa::launch_topk_rows(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route, s);
+      if (P.onchip) {
+        for (int n0 = na; n0 < na + Rc && e == hipSuccess; n0 += P.Rs) {
+          const int R = std::min(P.Rs, na + Rc - n0);
+          e = dsa::launch_idx_topk(D, q_idx, k_idx, n0, R, idx, rows_per_b, n_base, route,
+                                   w + P.it_off, s);
+        }
+      } else {
+        for (int n0 = na; n0 < na + Rc && e == hipSuccess; n0 += P.R) {
+          const int R = std::min(P.R, na + Rc - n0);
+          const int ncols = D.L - D.N + n0 + R;  // keys visible to the last row of the chunk
+          e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
+          if (e == hipSuccess)
+            e = dsa::launch_topk_rows(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route, s);
+        }
       }
       if (e != hipSuccess) break;
       dsa::AttnArgs a{};

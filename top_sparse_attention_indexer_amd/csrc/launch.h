@@ -22,6 +22,17 @@ hipError_t launch_indexer_tiles(const Dims& D, const void* q_idx, const void* k_
                                 int n0, int R, int ncols, float* out, size_t ld,
                                 bool write_masked, const uint8_t* route, hipStream_t s);
 
+// Indexer and exact top-K of query rows [n0, n0 + R) without a score matrix
+// (bf16 indexer inputs, d_idx in {32, 64, 128}, K <= 2048): MFMA scores
+// filtered against a sampled per-row threshold into candidate lists in `ws`
+// (idx_topk_ws_bytes), then the exact selection on the lists.  Index rows as
+// for launch_topk_rows.
+bool idx_topk_supported(const Dims& D);
+size_t idx_topk_ws_bytes(const Dims& D, int R);
+hipError_t launch_idx_topk(const Dims& D, const void* q_idx, const void* k_idx, int n0, int R,
+                           int32_t* topk, int idx_rows_per_b, int idx_n_base,
+                           const uint8_t* route, void* ws, hipStream_t s);
+
 // Streaming variant for few query rows per sequence (R <= 8): one thread per
 // key, every key row read once for all R rows.
 hipError_t launch_indexer_scan(const Dims& D, const void* q_idx, const void* k_idx,
