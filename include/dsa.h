@@ -140,6 +140,24 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx,
                              int32_t* topk_idx_out, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* dsa_fused_forward for callers that cannot allocate (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and results, but no workspace argument.  Scratch memory is a
+ * fixed 64 MiB device array inside the library (one per device, held until
+ * the process ends); problems whose dsa_fused_forward workspace exceeds it
+ * are rejected with DSA_ERR_WORKSPACE before anything is enqueued (decode
+ * batches fit; long prefills do not).  The call allocates nothing: the
+ * array's device address is looked up on the first call made on a device.
+ * Every call on a device shares that device's array, so calls that overlap
+ * on one device (other streams, other threads) race and must be ordered by
+ * the caller.  dsa_exec_status() takes the array's address as `ws`; it is
+ * not exposed, so that call does not apply here. */
+dsa_status dsa_fused_forward_noalloc(const dsa_problem* p, const void* q_idx,
+                                     const void* k_idx, const void* q, const void* k,
+                                     const void* v, const float* gate, const float* y2,
+                                     const uint8_t* route, float* out,
+                                     int32_t* topk_idx_out, void* stream);
+
 /* Execution status of the last dsa_fused_forward on workspace `ws`:
  * synchronises `stream` (the stream that call used), then returns
  * DSA_ERR_EXEC if that call was a single-launch decode and one of its waits

@@ -46,6 +46,8 @@ _SIGNATURES = {
                                        ctypes.c_size_t, _vp]),
     "dsa_fused_forward": (ctypes.c_int, [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, ctypes.c_size_t, _vp]),
+    "dsa_fused_forward_noalloc": (ctypes.c_int, [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _vp, _vp]),
     "dsa_exec_status": (ctypes.c_int, [_vp, _vp]),
     "dsa_set_wait_limit": (None, [ctypes.c_uint32]),
     "dsa_profile_start": (ctypes.c_int, [ctypes.c_int32]),
@@ -149,6 +151,13 @@ def dsa_fused_forward(p, q_idx, k_idx, q, k, v, gate, y2, route, out, topk_idx_o
     _check(lib().dsa_fused_forward(ctypes.byref(p), _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(gate), _ptr(y2), _ptr(route), _ptr(out),
                                    _ptr(topk_idx_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def dsa_fused_forward_noalloc(p, q_idx, k_idx, q, k, v, gate, y2, route, out,
+                              topk_idx_out=None, stream=None):
+    _check(lib().dsa_fused_forward_noalloc(ctypes.byref(p), _ptr(q_idx), _ptr(k_idx), _ptr(q),
+                                           _ptr(k), _ptr(v), _ptr(gate), _ptr(y2), _ptr(route),
+                                           _ptr(out), _ptr(topk_idx_out), _stream(stream)))
 
 
 def dsa_exec_status(ws, stream=None):

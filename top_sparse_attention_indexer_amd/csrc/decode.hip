@@ -47,7 +47,6 @@
 #include <atomic>
 #include <chrono>
 #include <cmath>
-#include <map>
 #include <mutex>
 
 #include <hip/hip_ext.h>
@@ -1642,21 +1641,30 @@ const void* select_kernel(const Dims& D) {
                     : pick_didx<float, float, 64>(D.didx, G);
 }
 
+// Occupancy per (kernel, device), cached in a fixed table: the library keeps
+// no static object whose destructor would run at process exit, and a call
+// after the first for a kernel allocates nothing.
+struct GridEntry {
+  const void* fn;
+  int dev, grid;
+};
+std::mutex g_grid_mu;
+GridEntry g_grid[128];
+int g_grid_n = 0;
+
 int coresident_blocks(const void* fn) {
-  static std::mutex mu;
-  static std::map<std::pair<const void*, int>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find({fn, dev});
-  if (it != cache.end()) return it->second;
+  std::lock_guard<std::mutex> lock(g_grid_mu);
+  for (int x = 0; x < g_grid_n; ++x)
+    if (g_grid[x].fn == fn && g_grid[x].dev == dev) return g_grid[x].grid;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, DT, 0) != hipSuccess) return 0;
   per = std::min(per, 2);
-  cache[{fn, dev}] = cus * per;
+  if (g_grid_n < 128) g_grid[g_grid_n++] = GridEntry{fn, dev, cus * per};
   return cus * per;
 }
 
@@ -1783,13 +1791,26 @@ std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
 
 // Epoch of the last decode launch per workspace (its control block sits at
 // the workspace's start), so that dsa_exec_status can tell this launch's
-// error word from one left by an earlier launch.
+// error word from one left by an earlier launch.  A fixed table of the last
+// kWsSlots workspaces (oldest replaced first).
+constexpr int kWsSlots = 64;
+struct WsEntry {
+  const void* ws;
+  uint32_t epoch;
+};
 std::mutex g_ws_mu;
-std::map<const void*, uint32_t> g_ws_epoch;
+WsEntry g_ws[kWsSlots];
+int g_ws_next = 0;
 
 void record_launch(const void* ws, uint32_t epoch) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  g_ws_epoch[ws] = epoch;
+  for (WsEntry& e : g_ws)
+    if (e.ws == ws) {
+      e.epoch = epoch;
+      return;
+    }
+  g_ws[g_ws_next] = WsEntry{ws, epoch};
+  g_ws_next = (g_ws_next + 1) % kWsSlots;
 }
 
 void set_wait_limit(uint32_t polls) { g_wait_limit.store(polls, std::memory_order_relaxed); }
@@ -1799,9 +1820,9 @@ int decode_exec_status(const void* ws, hipStream_t s, hipError_t* err) {
   uint32_t epoch = 0;
   {
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    auto it = g_ws_epoch.find(ws);
-    if (it == g_ws_epoch.end()) return 0;
-    epoch = it->second;
+    for (const WsEntry& e : g_ws)
+      if (e.ws == ws && ws) epoch = e.epoch;
+    if (epoch == 0) return 0;
   }
   *err = hipStreamSynchronize(s);
   if (*err != hipSuccess) return 0;
@@ -1813,7 +1834,18 @@ int decode_exec_status(const void* ws, hipStream_t s, hipError_t* err) {
 
 void forget_launch(const void* ws) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  g_ws_epoch.erase(ws);
+  for (WsEntry& e : g_ws)
+    if (e.ws == ws) e = WsEntry{nullptr, 0};
+}
+
+hipError_t decode_setup() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  StreamOrder& so = stream_order(dev);
+  std::lock_guard<std::mutex> lock(so.mu);
+  if (!so.done) e = hipEventCreateWithFlags(&so.done, hipEventDisableTiming);
+  return e;
 }
 
 hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, const void* k_idx,

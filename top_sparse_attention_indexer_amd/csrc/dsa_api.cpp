@@ -257,6 +257,23 @@ dsa_status check_gate(const float* gate, const float* y2) {
 
 }  // namespace
 
+namespace dsa {
+
+dsa_status fused_ws_need(const dsa_problem* p, size_t* bytes) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  *bytes = is_empty(D) ? 0 : plan_fused(D).total;
+  return ok();
+}
+
+dsa_status report(dsa_status st, const char* msg) {
+  if (st == DSA_OK) return ok();
+  return fail(st, "%s", msg);
+}
+
+}  // namespace dsa
+
 extern "C" {
 
 dsa_status dsa_workspace_size(const dsa_problem* p, size_t* bytes) {

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/dsa.h"
+
 namespace dsa {
 
 struct Dims {
@@ -126,6 +128,9 @@ constexpr uint32_t kDefaultWaitLimit = 1u << 24;
 void set_wait_limit(uint32_t polls);
 int decode_exec_status(const void* ws, hipStream_t s, hipError_t* err);
 void forget_launch(const void* ws);
+// Creates, on the current device, what the first decode launch would
+// otherwise create (the cross-stream ordering event).
+hipError_t decode_setup();
 
 // ---- stage timing (dsa_profile_start / dsa_profile_stop) -----------------------
 enum Stage { kStageIndexer = 0, kStageTopk = 1, kStageAttention = 2, kStageMerge = 3,
@@ -140,6 +145,13 @@ struct ProfScope {
   ProfScope(hipStream_t s_, int stage) : s(s_) { prof_begin(s, stage); }
   ~ProfScope() { prof_end(s); }
 };
+
+// ---- entry-point helpers (dsa_api.cpp) -----------------------------------------
+// Workspace bytes dsa_fused_forward needs for *p (checks *p like the entry
+// points; the plan the call will take, including the single-launch decode).
+dsa_status fused_ws_need(const dsa_problem* p, size_t* bytes);
+// Sets the thread's last-error message and returns st.
+dsa_status report(dsa_status st, const char* msg);
 
 // ---- misc ------------------------------------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s);

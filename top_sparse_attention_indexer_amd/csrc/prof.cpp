@@ -6,7 +6,6 @@
 
 #include <atomic>
 #include <mutex>
-#include <vector>
 
 #include "launch.h"
 
@@ -15,9 +14,12 @@ namespace {
 
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
-std::vector<hipEvent_t> g_ev;     // 2 per launch: begin, end
-std::vector<int> g_stage;         // stage of each pair
-std::vector<char> g_closed;       // end event recorded
+// plain arrays (created by prof_start, released by prof_stop), so that no
+// static object with a destructor is left for process exit
+hipEvent_t* g_ev = nullptr;       // 2 per launch: begin, end
+int* g_stage = nullptr;           // stage of each pair
+char* g_closed = nullptr;         // end event recorded
+size_t g_pairs = 0;               // capacity in pairs
 size_t g_used = 0;                // pairs recorded
 size_t g_dropped = 0;             // launches not recorded (pool full)
 thread_local long long t_open = -1;  // pair opened by this thread's last prof_begin
@@ -29,7 +31,7 @@ void prof_begin(hipStream_t s, int stage) {
   std::lock_guard<std::mutex> lock(g_mu);
   t_open = -1;
   if (!g_on.load(std::memory_order_relaxed)) return;
-  if (2 * (g_used + 1) > g_ev.size()) {
+  if (g_used + 1 > g_pairs) {
     ++g_dropped;
     return;
   }
@@ -47,18 +49,31 @@ void prof_end(hipStream_t s) {
   t_open = -1;
 }
 
+void prof_release() {
+  for (size_t k = 0; k < 2 * g_pairs; ++k)
+    if (g_ev[k]) (void)hipEventDestroy(g_ev[k]);
+  delete[] g_ev;
+  delete[] g_stage;
+  delete[] g_closed;
+  g_ev = nullptr;
+  g_stage = nullptr;
+  g_closed = nullptr;
+  g_pairs = g_used = g_dropped = 0;
+}
+
 hipError_t prof_start(int max_launches) {
   std::lock_guard<std::mutex> lock(g_mu);
-  for (hipEvent_t e : g_ev) (void)hipEventDestroy(e);
-  g_ev.clear();
-  g_stage.assign((size_t)max_launches, -1);
-  g_closed.assign((size_t)max_launches, 0);
-  g_used = g_dropped = 0;
-  for (int i = 0; i < 2 * max_launches; ++i) {
-    hipEvent_t e;
-    hipError_t err = hipEventCreate(&e);
-    if (err != hipSuccess) return err;
-    g_ev.push_back(e);
+  prof_release();
+  g_ev = new hipEvent_t[2 * (size_t)max_launches]();
+  g_stage = new int[max_launches]();
+  g_closed = new char[max_launches]();
+  g_pairs = (size_t)max_launches;
+  for (size_t k = 0; k < 2 * g_pairs; ++k) {
+    hipError_t err = hipEventCreate(&g_ev[k]);
+    if (err != hipSuccess) {
+      prof_release();
+      return err;
+    }
   }
   g_on.store(true, std::memory_order_relaxed);
   return hipSuccess;
@@ -85,11 +100,7 @@ hipError_t prof_stop(double* ms, int32_t* launches, int n_stages, long long* dro
     }
   }
   if (dropped) *dropped = (long long)g_dropped;
-  for (hipEvent_t e : g_ev) (void)hipEventDestroy(e);
-  g_ev.clear();
-  g_stage.clear();
-  g_closed.clear();
-  g_used = g_dropped = 0;
+  prof_release();
   return err;
 }
 
