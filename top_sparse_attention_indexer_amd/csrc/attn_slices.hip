@@ -46,6 +46,8 @@ constexpr int DROWS = 128;          // query rows per dense tile
 constexpr int DKEYS = 64;           // keys per dense step
 constexpr int kDenseLds = 4 * DKEYS * 256;   // K and V, double-buffered, 64 rows of <= 256 B
 constexpr int kSeg = 256;           // index entries staged per wave at a time
+// fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data)
+constexpr int kBufWord3 = 0x00020000;
 constexpr int kSparseLds = 4 * 2 * 32 * 256 + 4 * kSeg * 4;   // per wave: key and value tiles, entries
 constexpr int kLds = kDenseLds > kSparseLds ? kDenseLds : kSparseLds;
 
@@ -307,6 +309,9 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
           sacc[cc][u] = acc;
         }
       }
+      // raw scores; masks only where a key can lie past a row's position or
+      // the range (the wave's first row has the smallest position)
+      const bool interior = j0 + DKEYS - 1 <= off + rbase + w * 32 && j0 + DKEYS <= ke;
       bf16x8 pb[2][2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -316,35 +321,38 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int j = j0 + u * 16 + 4 * q + rr;
-            sv[u * 4 + rr] = (j <= prow[cc] && j < ke) ? sacc[cc][u][rr] * a.scale_log2 : -INFINITY;
+            sv[u * 4 + rr] = (interior || (j <= prow[cc] && j < ke)) ? sacc[cc][u][rr] : -INFINITY;
           }
         float mt = sv[0];
 #pragma unroll
         for (int x = 1; x < 16; ++x) mt = fmaxf(mt, sv[x]);
-        mt = max_xor16(mt);
-        mt = max_xor32(mt);
-        const float mnew = fmaxf(st[cc].m, mt);
-        float alpha = 1.f;
+        mt = max_xor32(max_xor16(mt)) * a.scale_log2;
+        // lazy maximum (see kLazyLog2)
+        const bool bump = mt > st[cc].m + kLazyLog2;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+          const float mnew = bump ? mt : st[cc].m;
+          const float alpha = exp2_fast(st[cc].m - mnew);
+#pragma unroll
+          for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) st[cc].o[dt][rr] *= alpha;
+          st[cc].l *= alpha;
+          st[cc].m = mnew;
+        }
         float pv[16];
-        if (mnew == -INFINITY) {
+        if (st[cc].m == -INFINITY) {
 #pragma unroll
           for (int x = 0; x < 16; ++x) pv[x] = 0.f;
         } else {
-          alpha = exp2_fast(st[cc].m - mnew);
 #pragma unroll
-          for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(sv[x] - mnew);
+          for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(fmaf(sv[x], a.scale_log2, -st[cc].m));
         }
         float ps = 0.f;
 #pragma unroll
         for (int x = 0; x < 16; ++x) ps += pv[x];
-        st[cc].l = st[cc].l * alpha + ps;
-        st[cc].m = mnew;
+        st[cc].l += ps;
         pb[cc][0] = pack8(pv);
         pb[cc][1] = pack8(pv + 8);
-#pragma unroll
-        for (int dt = 0; dt < HD / 16; ++dt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st[cc].o[dt][rr] *= alpha;
       }
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
@@ -382,7 +390,8 @@ template <int HD>
 __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, char* smem) {
   constexpr int T = HD / 32;
   constexpr int CPR = HD / 8;
-  constexpr int RPI = 64 / CPR;             // rows per wave load (16 B per lane)
+  constexpr int NG = 64 / CPR;              // lane groups (one 16-byte chunk per lane)
+  constexpr int RPG = 32 / NG;              // rows each lane group stages per step
   constexpr int TB = 32 * HD * 2;           // bytes of one 32-row tile
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, i = lane & 15;
@@ -390,9 +399,15 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
   char* ktile = smem + w * 2 * (32 * 256);
   char* vtile = ktile + TB;
   int* wl = reinterpret_cast<int*>(smem + 4 * 2 * 32 * 256) + w * kSeg;
-  const size_t rstride = (size_t)a.Hkv * HD;
   const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
   const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
+  // buffer resources over this (sequence, KV head)'s rows: 32-bit offsets,
+  // and a read past the last row returns zeros instead of faulting
+  const uint32_t rs_bytes = (uint32_t)(a.Hkv * HD * 2);
+  const int nrec = (int)((uint32_t)(a.L - 1) * rs_bytes + HD * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, kBufWord3);
+  const int gi = lane / CPR, ch = lane % CPR;
   const int kb = c * a.RC;
   const int r1 = min(a.R, r0 + kQB);
   const int nhc = (G + 15) / 16;
@@ -448,40 +463,53 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
         // register-staged pipeline: the 32 key and value rows of step e0 are
-        // loaded into registers (whole 256-byte rows per 16 lanes, the access
-        // pattern the L2 serves fastest) while step e0 - 32 computes, then
-        // written to the wave's LDS tiles (permuted as kt_swz / vt_swz) and
-        // read back as MFMA operands.  Entries of -1 read row 0 (masked).
-        u32x4 kr[32 / RPI], vr[32 / RPI];
+        // loaded into registers (whole 256-byte rows per lane group, the
+        // access pattern the L2 serves fastest; buffer loads with 32-bit
+        // offsets) while step e0 - 32 computes, then written to the wave's
+        // LDS tiles (permuted as kt_swz / vt_swz) and read back as MFMA
+        // operands.  Lane group gi = lane / CPR stages rows gi * RPG ..
+        // gi * RPG + RPG - 1.  Entries of -1 read row 0 (masked).
+        u32x4 kr[RPG], vr[RPG];
+        {
+          int jr[RPG];
 #pragma unroll
-        for (int m = 0; m < 32 / RPI; ++m) {
-          const int j = wl[m * RPI + lane / CPR];
-          const size_t jr = (size_t)(j < 0 ? 0 : j) * rstride + (lane % CPR) * 8;
-          kr[m] = *reinterpret_cast<const u32x4*>(kbase + jr);
-          vr[m] = *reinterpret_cast<const u32x4*>(vbase + jr);
+          for (int m = 0; m < RPG; m += 4)
+            *reinterpret_cast<int4*>(&jr[m]) = *reinterpret_cast<const int4*>(wl + gi * RPG + m);
+#pragma unroll
+          for (int m = 0; m < RPG; ++m) {
+            const uint32_t off = (uint32_t)max(jr[m], 0) * rs_bytes + ch * 16;
+            kr[m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+            vr[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+          }
         }
         for (int e0 = 0; e0 < sn; e0 += 32) {
           __builtin_amdgcn_s_waitcnt(0);   // this step's rows are in registers
 #pragma unroll
-          for (int m = 0; m < 32 / RPI; ++m) {
-            const int rr = m * RPI + lane / CPR, ch = lane % CPR;
+          for (int m = 0; m < RPG; ++m) {
+            const int rr = gi * RPG + m;
             *reinterpret_cast<u32x4*>(ktile + kt_swz<HD>(rr, ch)) = kr[m];
             *reinterpret_cast<u32x4*>(vtile + vt_swz<HD>(rr, ch * 16)) = vr[m];
           }
           bool kval[2][4];
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) kval[u][rr] = wl[e0 + u * 16 + 4 * q + rr] >= 0;
+          for (int u = 0; u < 2; ++u) {
+            const int4 e4 = *reinterpret_cast<const int4*>(wl + e0 + u * 16 + 4 * q);
+            kval[u][0] = e4.x >= 0; kval[u][1] = e4.y >= 0;
+            kval[u][2] = e4.z >= 0; kval[u][3] = e4.w >= 0;
+          }
           __builtin_amdgcn_s_waitcnt(0);   // tiles written
           __builtin_amdgcn_wave_barrier();
           if (e0 + 32 < sn) {
+            int jr[RPG];
 #pragma unroll
-            for (int m = 0; m < 32 / RPI; ++m) {
-              const int j = wl[e0 + 32 + m * RPI + lane / CPR];
-              const size_t jr = (size_t)(j < 0 ? 0 : j) * rstride + (lane % CPR) * 8;
-              kr[m] = *reinterpret_cast<const u32x4*>(kbase + jr);
-              vr[m] = *reinterpret_cast<const u32x4*>(vbase + jr);
+            for (int m = 0; m < RPG; m += 4)
+              *reinterpret_cast<int4*>(&jr[m]) =
+                  *reinterpret_cast<const int4*>(wl + e0 + 32 + gi * RPG + m);
+#pragma unroll
+            for (int m = 0; m < RPG; ++m) {
+              const uint32_t off = (uint32_t)max(jr[m], 0) * rs_bytes + ch * 16;
+              kr[m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+              vr[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
             }
           }
           step32_lds<HD>(ktile, vtile, qb, kval, a.scale_log2, st);
@@ -649,7 +677,9 @@ size_t slice_ws_bytes(const Dims& D, int R) {
 }
 
 bool slice_attention_supported(const Dims& D) {
-  return D.qkv_bf16 && (D.d == 64 || D.d == 128) && D.L <= 256 * kSliceKeys;
+  // 32-bit byte offsets within one sequence's keys (buffer loads)
+  return D.qkv_bf16 && (D.d == 64 || D.d == 128) && D.L <= 256 * kSliceKeys &&
+         (long long)D.L * D.Hkv * D.d * 2 < (1ll << 31);
 }
 
 hipError_t launch_attention_slices(const Dims& D, const AttnArgs& aa, void* ws, hipStream_t s) {

@@ -107,14 +107,22 @@ __device__ __forceinline__ int kt_swz(int R, int c16) {
   return R * (HD * 2) + ((c16 ^ (R & (CPR - 1))) << 4);
 }
 
+// Running maximum with a lazy update: the reference maximum m of a column
+// moves only when a new score exceeds it by more than kLazyLog2 (log2
+// units), so most steps skip the rescale of the accumulators.  Exact: every
+// weight is exp2(s - m) with the same m for numerator and denominator, and
+// bounded by 2^kLazyLog2 (fine for the fp32 sums and the bf16 P operand).
+constexpr float kLazyLog2 = 8.f;
+
 // 32-key step with both tiles in LDS (rows back to back, permuted as in
 // kt_swz / vt_swz): the key rows are read as the A operand (lane quad q
 // takes bytes 64 t + 16 q of its key row, the order the query operand uses),
-// the value rows with the transposing read.
+// the value rows with the transposing read.  Raw scores s; the scale c
+// (softmax scale * log2 e) enters through p = exp2(s * c - m).
 template <int HD>
 __device__ __forceinline__ void step32_lds(const char* ktile, const char* vtile,
                                            const bf16x8 (&qb)[HD / 32], const bool (&kvalid)[2][4],
-                                           float scale_log2, ColState<HD>& st) {
+                                           float c, ColState<HD>& st) {
   constexpr int T = HD / 32;
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, i = lane & 15;
@@ -129,29 +137,37 @@ __device__ __forceinline__ void step32_lds(const char* ktile, const char* vtile,
 #pragma unroll
     for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[t]), qb[t], acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[u * 4 + r] = kvalid[u][r] ? acc[r] * scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r) s[u * 4 + r] = kvalid[u][r] ? acc[r] : -INFINITY;
   }
   float mt = s[0];
 #pragma unroll
   for (int x = 1; x < 8; ++x) mt = fmaxf(mt, s[x]);
-  mt = max_xor16(mt);
-  mt = max_xor32(mt);
-  const float mnew = fmaxf(st.m, mt);
-  float alpha = 1.f;
+  mt = max_xor32(max_xor16(mt)) * c;
+  // lazy maximum: move only on a jump of more than kLazyLog2 (or the first
+  // finite score); the rescale runs only if some column of the wave moved
+  const bool bump = mt > st.m + kLazyLog2;
+  if (__builtin_amdgcn_ballot_w64(bump)) {
+    const float mnew = bump ? mt : st.m;
+    const float alpha = exp2_fast(st.m - mnew);   // 1 where unchanged, 0 from -inf
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.o[dt][r] *= alpha;
+    st.l *= alpha;
+    st.m = mnew;
+  }
   float p[8];
-  if (mnew == -INFINITY) {
+  if (st.m == -INFINITY) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) p[x] = 0.f;
   } else {
-    alpha = exp2_fast(st.m - mnew);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) p[x] = exp2_fast(s[x] - mnew);
+    for (int x = 0; x < 8; ++x) p[x] = exp2_fast(fmaf(s[x], c, -st.m));
   }
   float ps = 0.f;
 #pragma unroll
   for (int x = 0; x < 8; ++x) ps += p[x];
-  st.l = st.l * alpha + ps;
-  st.m = mnew;
+  st.l += ps;
   const bf16x8 pb = pack8(p);
   const int row0 = 4 * q + (i >> 2);
   const int colb = (i & 3) * 8;
@@ -161,10 +177,7 @@ __device__ __forceinline__ void step32_lds(const char* ktile, const char* vtile,
     const uint2 hi = lds_tr(vtile, vt_swz<HD>(16 + row0, dt * 32 + colb));
     uint4 u;
     u.x = lo.x; u.y = lo.y; u.z = hi.x; u.w = hi.y;
-    f32x4 o = st.o[dt];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] *= alpha;
-    st.o[dt] = mfma16(as_bf16x8(u), pb, o);
+    st.o[dt] = mfma16(as_bf16x8(u), pb, st.o[dt]);
   }
 }
 
