@@ -28,7 +28,10 @@ the design notes of the repository):
   * bottom-right causal alignment: query row n of N sits at absolute position
     p = L - N + n and sees keys 0..p (its own key included);
   * one indexer query per token and one indexer key per position, so the
-    selected set is shared by every head of the token ([HYB] §三);
+    selected set is shared by every head of the token ([HYB] §三); or, with
+    idx_heads > 1, one indexer query per (token, indexer head) and one set
+    per indexer head, query head h using set h // (Hq / idx_heads)
+    ([GDSA] §四.1 pseudo-code, top-k indices [batch, heads, top_k]);
   * the indexer score is a plain dot product (no scale, no RoPE, [GDSA] §二.2);
   * ties at the K-th score go to the lower position; -0.0 equals +0.0;
   * if the visible count is <= K every visible key is selected; index rows
@@ -118,32 +121,45 @@ def forward_row(b: int, n: int, *, n_q: int, kv_len: int, h_q: int, h_kv: int,
                 q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 gate: Optional[np.ndarray] = None, y2: Optional[np.ndarray] = None,
                 route: Optional[np.ndarray] = None,
-                softmax_scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """The whole path for query token (b, n): returns (out [Hq, d], idx [K]).
+                softmax_scale: Optional[float] = None,
+                idx_heads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """The whole path for query token (b, n): returns (out [Hq, d], idx).
 
     Steps in the order of [GDSA] §四.1: indexer scores, top-k, gather of the
     selected key/value rows, attention per head, gate blend.  Heads with
     route 0 attend to every visible key instead ([EA] §2.2, [HYB] §五.5).
     Rows whose heads are all dense skip the indexer; their index row is -1.
+
+    idx_heads = 1: one indexer query per token (q_idx [B, N, d_idx]) and one
+    selected set shared by every head; idx is [K].  idx_heads = H > 1: the
+    per-head selection of the [GDSA] §四.1 pseudo-code (scores and top-k
+    indices carry a head axis): q_idx is [B, N, H, d_idx], indexer head i
+    selects its own set from its own scores against the shared k_idx, and
+    query head h uses set h // (Hq / H); idx is [H, K].
     """
     vis = visible_count(n, n_q, kv_len)
     scale = 1.0 / math.sqrt(head_dim) if not softmax_scale or softmax_scale <= 0 else float(softmax_scale)
     group = h_q // h_kv
     sparse_heads = [h for h in range(h_q) if route is None or route[b, h] != 0]
-    idx = np.full(top_k, -1, dtype=np.int64)
+    nsets = max(1, idx_heads)
+    idx = np.full((nsets, top_k), -1, dtype=np.int64)
     if sparse_heads:
-        s = indexer_scores(q_idx[b, n], k_idx[b], vis)
-        idx = select_top_k(s, top_k)
-    selected = idx[idx >= 0]
+        for i in range(nsets):
+            qi = q_idx[b, n] if idx_heads <= 1 else q_idx[b, n, i]
+            idx[i] = select_top_k(indexer_scores(qi, k_idx[b], vis), top_k)
     out = np.zeros((h_q, head_dim), dtype=np.float64)
     for h in range(h_q):
         g_kv = h // group
-        rows = selected if h in sparse_heads else np.arange(vis)
+        if h in sparse_heads:
+            sel = idx[h // (h_q // nsets)]
+            rows = sel[sel >= 0]
+        else:
+            rows = np.arange(vis)
         a, _ = softmax_attention(q[b, n, h], k[b, rows, g_kv], v[b, rows, g_kv], scale)
         if gate is not None:
             a = gate_blend(a, float(gate[b, n, h]), y2[b, n, h])
         out[h] = a
-    return out, idx
+    return out, (idx[0] if idx_heads <= 1 else idx)
 
 
 def forward(params, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[int]] = None,
@@ -152,13 +168,16 @@ def forward(params, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[int]]
             ) -> Tuple[np.ndarray, np.ndarray]:
     """Run ``forward_row`` over the chosen (batch, row) pairs.
 
-    ``params`` carries batch, n_q, kv_len, h_q, h_kv, head_dim, top_k as
-    attributes.  Returns out [nb, nr, Hq, d] and idx [nb, nr, K].
+    ``params`` carries batch, n_q, kv_len, h_q, h_kv, head_dim, top_k (and
+    optionally idx_heads) as attributes.  Returns out [nb, nr, Hq, d] and
+    idx [nb, nr, K] ([nb, nr, H, K] with idx_heads = H > 1).
     """
     bs = list(range(params.batch)) if batches is None else list(batches)
     ns = list(range(params.n_q)) if rows is None else list(rows)
+    ih = getattr(params, "idx_heads", 1)
     out = np.zeros((len(bs), len(ns), params.h_q, params.head_dim), dtype=np.float64)
-    idx = np.zeros((len(bs), len(ns), params.top_k), dtype=np.int64)
+    ishape = (len(bs), len(ns), params.top_k) if ih <= 1 else (len(bs), len(ns), ih, params.top_k)
+    idx = np.zeros(ishape, dtype=np.int64)
     for i, b in enumerate(bs):
         for r, n in enumerate(ns):
             out[i, r], idx[i, r] = forward_row(
@@ -169,7 +188,7 @@ def forward(params, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[int]]
                 gate=inputs.get("gate") if use_gate else None,
                 y2=inputs.get("y2") if use_gate else None,
                 route=inputs.get("route") if use_route else None,
-                softmax_scale=softmax_scale)
+                softmax_scale=softmax_scale, idx_heads=ih)
     return out, idx
 
 

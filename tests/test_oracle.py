@@ -316,3 +316,48 @@ def test_synth_planted_rows():
     pos = x["planted"]
     assert len(np.unique(pos)) == 16
     assert np.max(np.abs(x["k_idx"][0, pos])) > 4 and np.max(np.abs(np.delete(x["k_idx"][0], pos, 0))) <= 4
+
+
+# --------------------------------------------------------------------------- per-head selection
+def _per_head(n_q, kv_len, h_q, h_kv, ih, k, seed):
+    w = synth.Workload("ph", 1, n_q, kv_len, h_q, h_kv, 16, 8, k, "fp32", "fp32", (-3, 3),
+                       seed=seed, idx_heads=ih)
+    return w, synth.make_inputs(w)
+
+
+@pytest.mark.parametrize("n_q,kv_len,h_q,h_kv,ih,k", [(5, 9, 4, 2, 4, 3), (3, 8, 4, 1, 2, 4),
+                                                      (6, 6, 8, 2, 8, 2), (1, 9, 4, 4, 4, 5)])
+def test_per_head_selection_matches_per_head_masked_sdpa(n_q, kv_len, h_q, h_kv, ih, k):
+    """Per-head top-k ([GDSA] §四.1 pseudo-code: indices [batch, heads, top_k]):
+    each indexer head's set is the brute-force top-k of its own exact integer
+    scores, and query head h attends over set h // (Hq / H), i.e. SDPA with a
+    per-head mask of that set."""
+    w, x = _per_head(n_q, kv_len, h_q, h_kv, ih, k, seed=8)
+    assert x["q_idx"].shape == (1, n_q, ih, 8)
+    out, idx = O.forward(w, x, use_gate=False)
+    assert idx.shape == (1, n_q, ih, k)
+    want = np.zeros_like(out[0])
+    for h in range(h_q):
+        mask = np.zeros((n_q, kv_len), bool)
+        for n in range(n_q):
+            vis = O.visible_count(n, n_q, kv_len)
+            s = x["k_idx"][0, :vis].astype(np.int64) @ x["q_idx"][0, n, h // (h_q // ih)].astype(np.int64)
+            sel = _brute_force_top_k(list(s), k)
+            assert idx[0, n, h // (h_q // ih)].tolist() == sel + [-1] * (k - len(sel))
+            mask[n, sel] = True
+        hk = h // (h_q // h_kv)
+        want[:, h] = _sdpa(x["q"][0][:, h:h + 1], x["k"][0][:, hk:hk + 1], x["v"][0][:, hk:hk + 1],
+                           mask)[:, 0]
+    np.testing.assert_allclose(out[0], want, rtol=0, atol=1e-12)
+
+
+def test_per_head_with_equal_queries_is_the_shared_selection():
+    """Every indexer head given the same query selects the shared set, and the
+    outputs equal those of the shared selection."""
+    w1, x1 = _small(7, 20, 8, 2, 16, 8, 5, seed=9)
+    wh = w1.replace(idx_heads=4)
+    xh = dict(x1, q_idx=np.repeat(x1["q_idx"][:, :, None, :], 4, axis=2))
+    o1, i1 = O.forward(w1, x1)
+    oh, ih = O.forward(wh, xh)
+    assert np.array_equal(ih, np.repeat(i1[:, :, None, :], 4, axis=2))
+    assert np.array_equal(oh, o1)

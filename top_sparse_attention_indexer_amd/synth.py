@@ -13,7 +13,8 @@ per-head full/sparse routing of the page "Elastic Attention：动态路由优化
 Recipe (one PCG64 stream per tensor, spawned from SeedSequence(seed) in the
 fixed order q_idx, k_idx, q, k, v, gate_z, y2, route, planted):
   * indexer entries: integers uniform on [lo, hi] inclusive, stored as float
-    (exact in bf16), so every indexer score is an exact integer;
+    (exact in bf16), so every indexer score is an exact integer; with
+    idx_heads > 1 every token has one indexer query per indexer head;
   * q, k, v, y2: N(0, 1) drawn in float32; q/k/v rounded to bf16 (round to
     nearest even) when the workload is bf16;
   * gate: z ~ N(0, 1) in float32, g = 1 / (1 + exp(-z)) evaluated in float64
@@ -54,6 +55,7 @@ class Workload:
     planted: int = 0
     planted_scale: int = 1
     seed: int = 0
+    idx_heads: int = 1  # indexer query heads (1: one selected set shared by all heads)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -109,7 +111,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
                 ) -> Dict[str, np.ndarray]:
     """Draw the inputs of workload ``w``.
 
-    Shapes: q_idx [B,N,d_idx], k_idx [B,L,d_idx], q [B,N,Hq,d],
+    Shapes: q_idx [B,N,d_idx] ([B,N,H_idx,d_idx] with idx_heads > 1),
+    k_idx [B,L,d_idx], q [B,N,Hq,d],
     k/v [B,L,Hkv,d], gate [B,N,Hq], y2 [B,N,Hq,d], route [B,Hq] (uint8).
     ``parts`` limits which tensors are drawn (each has its own stream, so a
     subset is identical to the same tensors of a full draw).  Planted rows
@@ -124,7 +127,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
     lo, hi = w.idx_range
     out: Dict[str, np.ndarray] = {}
     if "q_idx" in parts:
-        out["q_idx"] = rng["q_idx"].integers(lo, hi + 1, size=(B, N, w.idx_dim),
+        shape = (B, N, w.idx_dim) if w.idx_heads <= 1 else (B, N, w.idx_heads, w.idx_dim)
+        out["q_idx"] = rng["q_idx"].integers(lo, hi + 1, size=shape,
                                              dtype=np.int8).astype(np.float32)
     if "k_idx" in parts:
         k_idx = rng["k_idx"].integers(lo, hi + 1, size=(B, L, w.idx_dim),
