@@ -17,18 +17,22 @@
  *
  * Problem.  B sequences; each has L keys and its last N positions are the
  * queries (N <= L).  Query row n sits at position p = L - N + n and sees keys
- * 0..p (bottom-right causal alignment, own key included).  One indexer query
- * per token and one indexer key per position: the selected set is shared by
- * all heads of a token.  Query head h reads key/value head h / (Hq / Hkv).
+ * 0..p (bottom-right causal alignment, own key included).  One indexer key
+ * per position.  With idx_heads H <= 1 there is one indexer query per token
+ * and the selected set is shared by all heads of the token ([GDSA] §二.1).
+ * With H > 1 ([GDSA] §四.1, whose scores and indices carry a head axis) each
+ * token has H indexer queries, indexer head i selects its own set from its
+ * own scores, and query head h attends over set h / (Hq / H).  Query head h
+ * reads key/value head h / (Hq / Hkv).
  *
  * Layouts (all row-major, contiguous, every pointer 16-byte aligned):
- *   q_idx  [B, N, d_idx]      qidx dtype (fp32 or bf16)
+ *   q_idx  [B, N, H, d_idx]   qidx dtype (fp32 or bf16); H = max(1, idx_heads)
  *   k_idx  [B, L, d_idx]      qidx dtype
  *   q      [B, N, Hq, d]      qkv dtype
  *   k, v   [B, L, Hkv, d]     qkv dtype (token-major: one selected position
  *                             is one contiguous Hkv*d row)
- *   scores [B, N, L]          float32
- *   topk   [B, N, K]          int32, ascending, -1 padded
+ *   scores [B, N, H, L]       float32
+ *   topk   [B, N, H, K]       int32, ascending, -1 padded
  *   gate   [B, N, Hq]         float32, post-sigmoid g in [0, 1]
  *   y2     [B, N, Hq, d]      float32 second-branch output
  *   route  [B, Hq]            uint8, 1 = top-k sparse, 0 = full causal
@@ -91,21 +95,24 @@ typedef struct {
   int32_t qkv_dtype; /* dsa_dtype of q, k, v                                  */
   int32_t idx_dtype; /* dsa_dtype of q_idx, k_idx                             */
   float softmax_scale; /* <= 0 selects 1 / sqrt(head_dim)                     */
+  int32_t idx_heads; /* H >= 0 indexer heads; 0 or 1: one set per token shared
+                        by all heads; H > 1 (h_q a multiple of H): one set per
+                        indexer head, query head h using set h / (h_q / H)   */
 } dsa_problem;
 
 /* Bytes of workspace every entry point below accepts for problem *p
  * (the largest need of any of them).  Host-only; enqueues nothing. */
 dsa_status dsa_workspace_size(const dsa_problem* p, size_t* bytes);
 
-/* Indexer scores ([GDSA] §二.1-§二.2, [HYB] §三):
- *   scores[b,n,j] = sum_c q_idx[b,n,c] * k_idx[b,j,c]  for j <= p,
- *   scores[b,n,j] = -inf                               for j >  p.
+/* Indexer scores ([GDSA] §二.1-§二.2, [HYB] §三), per indexer head i:
+ *   scores[b,n,i,j] = sum_c q_idx[b,n,i,c] * k_idx[b,j,c]  for j <= p,
+ *   scores[b,n,i,j] = -inf                                 for j >  p.
  * Plain product, no scale, no rotary term, float32 accumulation (exact for
  * integer-valued inputs whose products sum below 2^24).  Needs no workspace. */
 dsa_status dsa_indexer_scores(const dsa_problem* p, const void* q_idx,
                               const void* k_idx, float* scores, void* stream);
 
-/* Top-K per query row ([GDSA] §二.1, [HYB] §三) from scores [B,N,L]:
+/* Top-K per index row ([GDSA] §二.1, [HYB] §三) from scores [B,N,H,L]:
  * the K_eff = min(K, p+1) visible positions with the largest score, ties to
  * the lower position, -0.0 equal to +0.0, written ascending and padded with
  * -1 to K.  Entries of scores beyond p are not read.  Selection compares the
@@ -116,7 +123,7 @@ dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t* topk_idx
 /* Attention over the selected rows plus gate ([HYB] §三, [AAM] §2.1,
  * [GDSA] §四.1 steps 3-5, [EA] §2.2):
  *   sparse head (route[b,h] = 1, or route == NULL):
- *     a = softmax_j(q . k_j * scale) v_j over j in topk_idx[b,n,:];
+ *     a = softmax_j(q . k_j * scale) v_j over j in topk_idx[b,n,h/(Hq/H),:];
  *     entries outside [0, p] (padding) are skipped; a row with no valid entry
  *     gives a = 0;
  *   dense head (route[b,h] = 0): the same over every j in 0..p, topk ignored;

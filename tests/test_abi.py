@@ -54,6 +54,8 @@ def test_workspace_size_and_problem_validation():
         (_p(qkv_dtype=7), B.DSA_ERR_UNSUPPORTED, "qkv_dtype"),
         (_p(idx_dtype=3), B.DSA_ERR_UNSUPPORTED, "idx_dtype"),
         (_p(softmax_scale=float("nan")), B.DSA_ERR_INVALID_ARG, "finite"),
+        (_p(idx_heads=-1), B.DSA_ERR_INVALID_ARG, "idx_heads"),
+        (_p(h_q=8, idx_heads=3), B.DSA_ERR_INVALID_ARG, "multiple of idx_heads"),
     ]
     for prob, status, msg in bad:
         assert lib.dsa_workspace_size(ctypes.byref(prob), ctypes.byref(n)) == status

@@ -28,11 +28,17 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+def idx_shape(w):
+    """[B, N, K], or [B, N, H, K] with H = idx_heads > 1 indexer heads."""
+    h = getattr(w, "idx_heads", 1)
+    return (w.batch, w.n_q, w.top_k) if h <= 1 else (w.batch, w.n_q, h, w.top_k)
+
+
 def run_fused(w, x, use_gate=True, use_route=True, want_idx=True, softmax_scale=0.0):
     p = B.problem_for(w, softmax_scale)
     dev = to_device(w, x)
     out = torch.empty((w.batch, w.n_q, w.h_q, w.head_dim), dtype=torch.float32, device="cuda")
-    idx = (torch.full((w.batch, w.n_q, w.top_k), -7, dtype=torch.int32, device="cuda")
+    idx = (torch.full(idx_shape(w), -7, dtype=torch.int32, device="cuda")
            if want_idx else None)
     ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
     B.dsa_fused_forward(p, dev["q_idx"], dev["k_idx"], dev["q"], dev["k"], dev["v"],
@@ -58,13 +64,16 @@ def check_rows(w, x, out, idx, rows, use_gate=True, use_route=True, batches=None
 
 
 def check_index_structure(w, idx, batches=None):
-    """Every row: ascending ids in [0, p], count min(K, vis), then -1 padding."""
+    """Every row (of every indexer head): ascending ids in [0, p], count
+    min(K, vis), then -1 padding."""
     N, L, K = w.n_q, w.kv_len, w.top_k
+    H = max(1, getattr(w, "idx_heads", 1))
     vis = torch.arange(N, device="cuda", dtype=torch.int64) + (L - N + 1)
+    vis = vis.repeat_interleave(H)
     cnt = torch.clamp(vis, max=K)
     pos = torch.arange(K, device="cuda")
     for b in (range(w.batch) if batches is None else batches):
-        t = idx[b].to(torch.int64)
+        t = idx[b].reshape(N * H, K).to(torch.int64)
         valid = pos[None, :] < cnt[:, None]
         assert torch.all(torch.where(valid, t >= 0, t == -1)).item()
         assert torch.all(torch.where(valid, t < vis[:, None], True)).item()
@@ -495,3 +504,76 @@ def test_sparse_attn_entry_with_oracle_indices(N, L, K, route_p, announce):
                       out, ws)
     torch.cuda.synchronize()
     assert np.max(np.abs(out.cpu().numpy() - want_out)) <= TOL["bf16"]
+
+
+# --------------------------------------------------------------------------- per-head selection
+# One indexer query per (token, indexer head) and one selected set per indexer
+# head; query head h attends over set h / (Hq / idx_heads).
+PER_HEAD = [
+    # the 8-sequence decode shape (32 query, 8 KV heads) at a 32K context: sets
+    # spanning two KV heads, and one set per query head
+    ("decode_b8_ctx32k_ih4", synth.WORKLOADS["decode_b8_ctx128k"].replace(
+        kv_len=32768, idx_heads=4)),
+    ("decode_b8_ctx32k_ih32", synth.WORKLOADS["decode_b8_ctx128k"].replace(
+        kv_len=32768, idx_heads=32)),
+    # 2 tokens x 4 heads = 8 index rows: streaming indexer and split-row top-k
+    ("spec_decode_ih4", _w(2, 2, 20000, 8, 2, 128, 64, 300).replace(idx_heads=4)),
+    # prefill over several key ranges (key-range attention, on-chip indexer)
+    ("prefill_ih2_mixed_route", _w(1, 600, 9000, 8, 2, 128, 64, 512, route_p=0.6,
+                                   seed=31).replace(idx_heads=2)),
+    ("prefill_ih8_one_set_per_head", _w(2, 300, 5000, 8, 4, 64, 32, 256,
+                                        seed=32).replace(idx_heads=8)),
+    # float32: score matrix, row top-k and the VALU attention
+    ("prefill_fp32_ih2", _w(1, 70, 500, 4, 2, 64, 32, 40, dt="fp32").replace(idx_heads=2)),
+    ("K_ge_L_ih4", _w(1, 64, 64, 4, 1, 64, 32, 128).replace(idx_heads=4)),
+]
+
+
+@pytest.mark.parametrize("name,w", PER_HEAD, ids=[e[0] for e in PER_HEAD])
+def test_per_head_selection(name, w, announce):
+    x = synth.make_inputs(w)
+    announce(f"fused_forward per-head {name} {w}")
+    out, idx = run_fused(w, x)
+    sparse_seqs = [b for b in range(w.batch) if x["route"][b].any()]
+    check_index_structure(w, idx, batches=sparse_seqs)
+    rows = list(range(w.n_q)) if w.n_q <= 80 else synth.sample_rows(w, 24).tolist()
+    check_rows(w, x, out, idx, rows=rows)
+    # the sets differ between indexer heads (else the test would not tell them apart)
+    if w.kv_len > w.top_k:
+        t = idx[sparse_seqs[0], -1]
+        assert not all(torch.equal(t[0], t[i]) for i in range(1, t.shape[0]))
+
+
+def test_per_head_entry_points(announce):
+    """dsa_indexer_scores -> dsa_topk -> dsa_sparse_attn with four indexer
+    heads: scores [B,N,H,L] exact, index rows exact, outputs within tolerance."""
+    w = _w(2, 40, 300, 8, 2, 128, 64, 32, route_p=0.7, seed=33).replace(idx_heads=4)
+    x = synth.make_inputs(w)
+    dev = to_device(w, x)
+    p = B.problem_for(w)
+    H = w.idx_heads
+    announce(f"indexer/topk/sparse_attn per-head {w}")
+    scores = torch.empty((w.batch, w.n_q, H, w.kv_len), dtype=torch.float32, device="cuda")
+    B.dsa_indexer_scores(p, dev["q_idx"], dev["k_idx"], scores)
+    ws = torch.empty(max(1, B.dsa_workspace_size(p)), dtype=torch.uint8, device="cuda")
+    idx = torch.full(idx_shape(w), -7, dtype=torch.int32, device="cuda")
+    B.dsa_topk(p, scores, idx, ws)
+    out = torch.empty((w.batch, w.n_q, w.h_q, w.head_dim), dtype=torch.float32, device="cuda")
+    B.dsa_sparse_attn(p, dev["q"], dev["k"], dev["v"], idx, dev["gate"], dev["y2"],
+                      dev["route"], out, ws)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    L, N = w.kv_len, w.n_q
+    for b in range(w.batch):
+        for n in range(N):
+            vis = L - N + n + 1
+            for i in range(H):
+                want = O.indexer_scores(x["q_idx"][b, n, i], x["k_idx"][b], vis)
+                assert np.array_equal(got[b, n, i, :vis], want[:vis].astype(np.float32))
+                assert np.all(np.isneginf(got[b, n, i, vis:]))
+    # the index rows of every head (route does not enter the top-k call)
+    want_out, want_idx = O.forward(w, x, use_route=False)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    want_out, _ = O.forward(w, x)
+    err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - want_out))
+    assert err <= TOL[w.qkv_dtype], f"max-abs error {err}"

@@ -26,7 +26,7 @@ class DsaProblem(ctypes.Structure):
                 ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("idx_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("idx_dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("idx_heads", ctypes.c_int32)]
 
 
 class DsaError(RuntimeError):
@@ -82,16 +82,17 @@ def lib() -> ctypes.CDLL:
 
 
 def problem(batch, n_q, kv_len, h_q, h_kv, head_dim, idx_dim, top_k,
-            qkv_dtype="bf16", idx_dtype="bf16", softmax_scale=0.0) -> DsaProblem:
+            qkv_dtype="bf16", idx_dtype="bf16", softmax_scale=0.0, idx_heads=1) -> DsaProblem:
     dt = {"fp32": DSA_FP32, "bf16": DSA_BF16, DSA_FP32: DSA_FP32, DSA_BF16: DSA_BF16}
     return DsaProblem(batch, n_q, kv_len, h_q, h_kv, head_dim, idx_dim, top_k,
-                      dt.get(qkv_dtype, qkv_dtype), dt.get(idx_dtype, idx_dtype), softmax_scale)
+                      dt.get(qkv_dtype, qkv_dtype), dt.get(idx_dtype, idx_dtype), softmax_scale,
+                      idx_heads)
 
 
 def problem_for(w, softmax_scale: float = 0.0) -> DsaProblem:
     """Problem of any object carrying the workload attributes."""
     return problem(w.batch, w.n_q, w.kv_len, w.h_q, w.h_kv, w.head_dim, w.idx_dim, w.top_k,
-                   w.qkv_dtype, w.idx_dtype, softmax_scale)
+                   w.qkv_dtype, w.idx_dtype, softmax_scale, getattr(w, "idx_heads", 1))
 
 
 def _check(status: int):

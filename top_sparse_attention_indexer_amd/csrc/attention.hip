@@ -31,7 +31,7 @@ __global__ __launch_bounds__(AT) void k_attn(
     const int32_t* __restrict__ topk, int idx_rows_per_b, int idx_n_base,
     const float* __restrict__ gate, const float* __restrict__ y2, const uint8_t* __restrict__ route,
     float* __restrict__ out, float* __restrict__ part, int N, int L, int Hq, int Hkv, int K,
-    int n0, int R, int splits, int split_stride, int dense_mode, float scale_log2) {
+    int n0, int R, int splits, int split_stride, int dense_mode, float scale_log2, int IH) {
   // blockIdx.x = ((b * R + r) * Hkv + g) * splits + s
   const int s = blockIdx.x % splits;
   const int item = blockIdx.x / splits;
@@ -75,15 +75,20 @@ __global__ __launch_bounds__(AT) void k_attn(
     e0 = s * per;
     e1 = min(K, e0 + per);
   }
-  const int32_t* irow = topk ? topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K : nullptr;
+  // index rows of this token: one per indexer head (IH), query head h using
+  // row h / (Hq / IH); a pass over heads stays within one row
+  const int32_t* trow = topk ? topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * IH * K : nullptr;
+  const int HPS = Hq / IH;
 
   constexpr int CPT = HB * HD / AT;        // accumulators per thread
   constexpr int HSTEP = AT / HD;           // head stride between a thread's accumulators
   const int c_own = threadIdx.x % HD;
   const int h_own = threadIdx.x / HD;
 
-  for (int hc = 0; hc < nact; hc += HB) {
-    const int nh = min(HB, nact - hc);
+  for (int hc = 0, nh = 0; hc < nact; hc += nh) {
+    nh = 1;
+    while (nh < HB && hc + nh < nact && act[hc + nh] / HPS == act[hc] / HPS) ++nh;
+    const int32_t* irow = trow ? trow + (size_t)(act[hc] / HPS) * K : nullptr;
     for (int e = threadIdx.x; e < HB * HD; e += AT) {
       const int hh = e / HD, c = e - hh * HD;
       float x = 0.f;
@@ -264,7 +269,7 @@ hipError_t attn_launch(const Dims& D, const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_attn<T, HD>), dim3((unsigned)blocks), dim3(AT), 0, s, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, a.topk, a.idx_rows_per_b, a.idx_n_base,
                        a.gate, a.y2, a.route, a.out, a.part, D.N, D.L, D.Hq, D.Hkv, D.K, a.n0, a.R,
-                       splits, stride, mode, sl2);
+                       splits, stride, mode, sl2, D.IH);
   }
   if (stride > 1) {
     const size_t blocks = (size_t)D.B * a.R * D.Hq;

@@ -413,7 +413,9 @@ __global__ __launch_bounds__(MT, WORK == kSparseWork ? 3 : 2) void k_attn_mfma(M
 }  // namespace
 
 bool mfma_attention_supported(const Dims& D) {
-  return D.qkv_bf16 && (D.d == 64 || D.d == 128) && D.K <= 2048 && D.Hq / D.Hkv >= 1;
+  // one selected set per token (per-head sets take the other kernels)
+  return D.qkv_bf16 && (D.d == 64 || D.d == 128) && D.K <= 2048 && D.Hq / D.Hkv >= 1 &&
+         D.IH == 1;
 }
 
 hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& aa, hipStream_t s) {

@@ -66,6 +66,7 @@ struct SliceArgs {
   int RC, NC;           // keys per range; ranges seen by the chunk's last row
   int cap;              // slices per queue table
   float scale_log2;
+  int IH;               // index rows per token (indexer heads); head h uses h / (Hq / IH)
 };
 
 // Queue tables: [0, 8) slice counts, [8, 16) item totals, then per queue the
@@ -141,22 +142,26 @@ __global__ __launch_bounds__(ST) void k_sched(SliceArgs a, int32_t* sched) {
   }
 }
 
-// One wave per index row: offsets of the ranges in the row.  off[c] = number
-// of valid entries (in [0, p]) below c * RC, for c = 0 .. nr (nr = p / RC + 1);
-// for ascending rows the entries of range c are [off[c], off[c + 1]).
+// One wave per index row (token row and indexer head): offsets of the ranges
+// in the row.  off[c] = number of valid entries (in [0, p]) below c * RC,
+// for c = 0 .. nr (nr = p / RC + 1); for ascending rows the entries of range
+// c are [off[c], off[c + 1]).
 __global__ __launch_bounds__(ST) void k_range_offsets(SliceArgs a) {
   __shared__ int hist[4][257];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const long long row = (long long)blockIdx.x * 4 + w;
-  if (row >= (long long)a.B * a.R) return;   // wave-uniform; no block barrier below
-  const int b = (int)(row / a.R), r = (int)(row - (long long)b * a.R);
+  const long long row = (long long)blockIdx.x * 4 + w;   // ((b * R + r) * IH + ih)
+  if (row >= (long long)a.B * a.R * a.IH) return;   // wave-uniform; no block barrier below
+  const int ih = (int)(row % a.IH);
+  const long long br = row / a.IH;
+  const int b = (int)(br / a.R), r = (int)(br - (long long)b * a.R);
   const int n = a.n0 + r, p = a.L - a.N + n;
   const int nr = p / a.RC + 1;
   int* h = hist[w];
   for (int c = lane; c <= nr; c += 64) h[c] = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  const int32_t* irow = a.topk + ((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.K;
+  const int32_t* irow =
+      a.topk + (((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.IH + ih) * a.K;
   for (int e = lane; e < a.K; e += 64) {
     const int j = irow[e];
     if (j >= 0 && j <= p) atomicAdd(&h[j / a.RC + 1], 1);
@@ -410,19 +415,24 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
   const int gi = lane / CPR, ch = lane % CPR;
   const int kb = c * a.RC;
   const int r1 = min(a.R, r0 + kQB);
-  const int nhc = (G + 15) / 16;
+  const int HPS = a.Hq / a.IH;              // query heads per index row
   for (int r = r0 + w; r < r1; r += 4) {
     const int n = a.n0 + r, p = a.L - a.N + n;
     const int ke = min(kb + a.RC, p + 1);
     const int nr = p / a.RC + 1;
-    const int32_t* orow = a.off + ((size_t)b * a.R + r) * (a.NC + 1);
-    const int lo = min(max(orow[c], 0), a.K);
-    const int hi = min(max(orow[c + 1], lo), a.K);
-    const int32_t* irow = a.topk + ((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.K;
-    for (int hc = 0; hc < nhc; ++hc) {
+    // heads of the group by index row (set ih = h / HPS), up to 16 per chunk
+    for (int h0 = g * G; h0 < g * G + G;) {
+      const int ih = h0 / HPS;
+      const int hend = min(g * G + G, (ih + 1) * HPS);
+      const int hc0 = h0;
+      h0 = min(hend, hc0 + 16);
+      const int32_t* orow = a.off + (((size_t)b * a.R + r) * a.IH + ih) * (a.NC + 1);
+      const int lo = min(max(orow[c], 0), a.K);
+      const int hi = min(max(orow[c + 1], lo), a.K);
+      const int32_t* irow =
+          a.topk + (((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.IH + ih) * a.K;
       int myh = -1, cnt = 0;
-      for (int x = hc * 16; x < min(G, hc * 16 + 16); ++x) {
-        const int h = g * G + x;
+      for (int h = hc0; h < h0; ++h) {
         if (head_sparse(a, b, h)) {
           if (cnt == i) myh = h;
           ++cnt;
@@ -668,7 +678,7 @@ size_t slice_ws_bytes(const Dims& D, int R) {
   const SlicePlan P = slice_plan(D, R);
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t b = 0;
-  b += al((size_t)D.B * R * (P.NC + 1) * 4);                      // offsets
+  b += al((size_t)D.B * R * D.IH * (P.NC + 1) * 4);              // offsets
   b += al((16 + (size_t)2 * kXcd * P.cap) * 4);                   // queue tables
   b += al(kXcd * 4 * 16);                                         // counters
   b += al((size_t)D.B * R * P.NC * D.Hq * D.d * 4);               // partial outputs
@@ -696,16 +706,17 @@ hipError_t launch_attention_slices(const Dims& D, const AttnArgs& aa, void* ws, 
   a.NC = (D.L - D.N + aa.n0 + aa.R - 1) / P.RC + 1;
   a.cap = P.cap;
   a.scale_log2 = D.scale * kLog2e;
+  a.IH = D.IH;
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   char* w = (char*)ws;
   size_t o = 0;
-  a.off = (const int32_t*)(w + o);   o += al((size_t)D.B * aa.R * (P.NC + 1) * 4);
+  a.off = (const int32_t*)(w + o);   o += al((size_t)D.B * aa.R * D.IH * (P.NC + 1) * 4);
   int32_t* sched = (int32_t*)(w + o); o += al((16 + (size_t)2 * kXcd * P.cap) * 4);
   a.sched = sched;
   a.ctr = (uint32_t*)(w + o);        o += al(kXcd * 4 * 16);
   a.part_o = (float*)(w + o);        o += al((size_t)D.B * aa.R * P.NC * D.Hq * D.d * 4);
   a.part_lse = (float*)(w + o);
-  const long long rows = (long long)D.B * aa.R;
+  const long long rows = (long long)D.B * aa.R * D.IH;   // index rows
   {
     ProfScope ps(s, kStagePrep);
     hipLaunchKernelGGL(k_range_offsets, dim3((unsigned)((rows + 3) / 4)), dim3(ST), 0, s, a);

@@ -1672,6 +1672,7 @@ int coresident_blocks(const void* fn) {
 
 bool decode_plan(const Dims& D, int grid, DecodePlan& P) {
   if (D.N < 1 || D.N > 4 || grid <= 0 || grid > kMaxGrid) return false;
+  if (D.IH != 1) return false;   // one selected set per token only
   const int rows = D.B * D.N;
   if (rows > grid) return false;
   // smallest chunk (multiple of 256) with one unit per workgroup

@@ -63,6 +63,12 @@ dsa_status check_problem(const dsa_problem* p, dsa::Dims& D) {
     return fail(DSA_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
   if ((long long)p->h_q * p->head_dim > (1ll << 20))
     return fail(DSA_ERR_UNSUPPORTED, "h_q * head_dim too large");
+  if (p->idx_heads < 0) return fail(DSA_ERR_INVALID_ARG, "idx_heads must be >= 0");
+  const int ih = p->idx_heads > 1 ? p->idx_heads : 1;
+  if (p->h_q % ih != 0)
+    return fail(DSA_ERR_INVALID_ARG, "h_q (%d) is not a multiple of idx_heads (%d)", p->h_q, ih);
+  if ((long long)p->n_q * ih > (1ll << 30))
+    return fail(DSA_ERR_UNSUPPORTED, "n_q * idx_heads too large");
   D.B = p->batch;
   D.N = p->n_q;
   D.L = p->kv_len;
@@ -74,10 +80,15 @@ dsa_status check_problem(const dsa_problem* p, dsa::Dims& D) {
   D.qkv_bf16 = p->qkv_dtype == DSA_BF16;
   D.idx_bf16 = p->idx_dtype == DSA_BF16;
   D.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  D.IH = ih;
   return DSA_OK;
 }
 
 bool is_empty(const dsa::Dims& D) { return D.B == 0 || D.N == 0; }
+
+// The indexer and top-k stages see IH index rows per query token; few such
+// rows take the streaming indexer and the split-row top-k.
+bool few_index_rows(const dsa::Dims& D) { return (long long)D.N * D.IH <= kDecodeRows; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -87,7 +98,7 @@ struct Plan {
   dsa::DecodePlan dp;
   size_t dec_off = 0, dec_bytes = 0;
   bool decode;     // streaming indexer + split-row top-k
-  int R;           // query rows per chunk
+  int R;           // query tokens per chunk (times IH index rows)
   size_t scores_off = 0, scores_bytes = 0, ld = 0;
   size_t tk_off = 0, tk_bytes = 0;      // split top-k scratch
   size_t idx_off = 0, idx_bytes = 0;    // internal index rows of one chunk
@@ -96,7 +107,7 @@ struct Plan {
   bool slices = false;  // key-range blocked MFMA attention (prefill, bf16)
   int Ra = 0;           // query rows per attention launch on that path
   bool onchip = false;  // indexer + top-k without a score matrix
-  int Rs = 0;           // query rows per launch of that pair
+  int Rs = 0;           // query tokens per launch of that pair
   size_t it_off = 0, it_bytes = 0;
   size_t sl_off = 0, sl_bytes = 0;
   size_t total = 0;
@@ -116,7 +127,7 @@ int sparse_heads_per_item(const dsa::Dims& D) {
 }
 
 int prefill_chunk_rows(const dsa::Dims& D) {
-  size_t per_row = (size_t)D.B * D.L;
+  size_t per_row = (size_t)D.B * D.L * D.IH;
   size_t r = std::max<size_t>(64, kScoreBudget / std::max<size_t>(per_row, 1));
   r = r / 64 * 64;
   return (int)std::min<size_t>(r, (size_t)D.N);
@@ -139,9 +150,9 @@ bool use_slices(const dsa::Dims& D) {
 
 Plan plan_topk(const dsa::Dims& D) {
   Plan P;
-  P.decode = D.N <= kDecodeRows;
+  P.decode = few_index_rows(D);
   P.R = D.N;
-  if (P.decode) P.tk_bytes = dsa::split_topk_ws_bytes(D, D.N);
+  if (P.decode) P.tk_bytes = dsa::split_topk_ws_bytes(D, D.N * D.IH);
   P.total = align256(P.tk_bytes);
   return P;
 }
@@ -166,7 +177,7 @@ Plan plan_attn(const dsa::Dims& D) {
 // Few query rows: the single-launch decode kernel when its grid and LDS limits
 // allow (needs a device to size the co-resident grid).
 bool plan_fused_decode(const dsa::Dims& D, Plan& P) {
-  if (D.N > 4) return false;
+  if (D.N > 4 || D.IH != 1) return false;
   const int grid = dsa::decode_grid(D);
   if (grid <= 0 || !dsa::decode_plan(D, grid, P.dp)) return false;
   P.fused_decode = true;
@@ -186,7 +197,7 @@ bool plan_fused_decode(const dsa::Dims& D, Plan& P) {
 Plan plan_fused(const dsa::Dims& D, bool allow_single_launch = true) {
   Plan P;
   if (allow_single_launch && plan_fused_decode(D, P)) return P;
-  P.decode = D.N <= kDecodeRows;
+  P.decode = few_index_rows(D);
   P.slices = use_slices(D);
   P.Ra = P.slices ? slice_chunk_rows(D) : D.N;
   P.onchip = P.slices && dsa::idx_topk_supported(D);
@@ -195,23 +206,23 @@ Plan plan_fused(const dsa::Dims& D, bool allow_single_launch = true) {
   size_t off = 0;
   if (P.onchip) {
     // candidate lists of up to kCandBudget bytes per launch
-    const size_t per_row = dsa::idx_topk_ws_bytes(D, 1);
+    const size_t per_row = dsa::idx_topk_ws_bytes(D, D.IH);
     P.Rs = (int)std::min<size_t>((size_t)P.Ra, std::max<size_t>(64, kCandBudget / per_row));
     P.it_off = off;
-    P.it_bytes = dsa::idx_topk_ws_bytes(D, P.Rs);
+    P.it_bytes = dsa::idx_topk_ws_bytes(D, P.Rs * D.IH);
     off = align256(off + P.it_bytes);
   } else {
     P.scores_off = off;
-    P.scores_bytes = (size_t)D.B * P.R * D.L * sizeof(float);
+    P.scores_bytes = (size_t)D.B * P.R * D.IH * D.L * sizeof(float);
     off = align256(off + P.scores_bytes);
   }
   if (P.decode) {
     P.tk_off = off;
-    P.tk_bytes = dsa::split_topk_ws_bytes(D, P.R);
+    P.tk_bytes = dsa::split_topk_ws_bytes(D, P.R * D.IH);
     off = align256(off + P.tk_bytes);
   }
   P.idx_off = off;
-  P.idx_bytes = (size_t)D.B * (P.slices ? P.Ra : P.R) * D.K * sizeof(int32_t);
+  P.idx_bytes = (size_t)D.B * (P.slices ? P.Ra : P.R) * D.IH * D.K * sizeof(int32_t);
   off = align256(off + P.idx_bytes);
   if (P.slices) {
     P.sl_off = off;
@@ -304,10 +315,11 @@ dsa_status dsa_indexer_scores(const dsa_problem* p, const void* q_idx, const voi
   DSA_NEED(scores, "scores");
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (D.N <= kDecodeRows)
-    e = dsa::launch_indexer_scan(D, q_idx, k_idx, 0, D.N, D.L, scores, (size_t)D.L, true, nullptr, s);
+  const int rows = D.N * D.IH;   // index rows per sequence
+  if (few_index_rows(D))
+    e = dsa::launch_indexer_scan(D, q_idx, k_idx, 0, rows, D.L, scores, (size_t)D.L, true, nullptr, s);
   else
-    e = dsa::launch_indexer_tiles(D, q_idx, k_idx, 0, D.N, D.L, scores, (size_t)D.L, true, nullptr, s);
+    e = dsa::launch_indexer_tiles(D, q_idx, k_idx, 0, rows, D.L, scores, (size_t)D.L, true, nullptr, s);
   return hip_status(e, "dsa_indexer_scores");
 }
 
@@ -323,11 +335,12 @@ dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t* topk_idx
   if ((st = check_ws(P, ws, ws_bytes)) != DSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
+  const int rows = D.N * D.IH;   // index rows per sequence
   if (P.decode)
-    e = dsa::launch_topk_split(D, scores, (size_t)D.L, 0, D.N, topk_idx, D.N, 0, nullptr,
+    e = dsa::launch_topk_split(D, scores, (size_t)D.L, 0, rows, topk_idx, rows, 0, nullptr,
                                (char*)ws + P.tk_off, s);
   else
-    e = dsa::launch_topk_rows(D, scores, (size_t)D.L, 0, D.N, topk_idx, D.N, 0, nullptr, s);
+    e = dsa::launch_topk_rows(D, scores, (size_t)D.L, 0, rows, topk_idx, rows, 0, nullptr, s);
   return hip_status(e, "dsa_topk");
 }
 
@@ -367,7 +380,7 @@ dsa_status dsa_sparse_attn(const dsa_problem* p, const void* q, const void* k, c
   a.n0 = 0; a.R = D.N;
   a.splits_sparse = P.splits_sparse;
   a.splits_dense = P.splits_dense;
-  if (!P.decode && dsa::mfma_attention_supported(D))
+  if (D.N > kDecodeRows && dsa::mfma_attention_supported(D))
     return hip_status(dsa::launch_attention_mfma(D, a, (hipStream_t)stream), "dsa_sparse_attn");
   return hip_status(dsa::launch_attention(D, a, (hipStream_t)stream), "dsa_sparse_attn");
 }
@@ -414,19 +427,23 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
       int32_t* idx = topk_idx_out ? topk_idx_out : idx_chunk;
       const int rows_per_b = topk_idx_out ? D.N : P.Ra;
       const int n_base = topk_idx_out ? 0 : na;
+      // the indexer and top-k count index rows (IH per token)
+      const int H = D.IH;
       if (P.onchip) {
         for (int n0 = na; n0 < na + Rc && e == hipSuccess; n0 += P.Rs) {
           const int R = std::min(P.Rs, na + Rc - n0);
-          e = dsa::launch_idx_topk(D, q_idx, k_idx, n0, R, idx, rows_per_b, n_base, route,
-                                   w + P.it_off, s);
+          e = dsa::launch_idx_topk(D, q_idx, k_idx, n0 * H, R * H, idx, rows_per_b * H,
+                                   n_base * H, route, w + P.it_off, s);
         }
       } else {
         for (int n0 = na; n0 < na + Rc && e == hipSuccess; n0 += P.R) {
           const int R = std::min(P.R, na + Rc - n0);
           const int ncols = D.L - D.N + n0 + R;  // keys visible to the last row of the chunk
-          e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
+          e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0 * H, R * H, ncols, scores, P.ld, false,
+                                        route, s);
           if (e == hipSuccess)
-            e = dsa::launch_topk_rows(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route, s);
+            e = dsa::launch_topk_rows(D, scores, P.ld, n0 * H, R * H, idx, rows_per_b * H,
+                                      n_base * H, route, s);
         }
       }
       if (e != hipSuccess) break;
@@ -446,15 +463,19 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
     int32_t* idx = topk_idx_out ? topk_idx_out : idx_chunk;
     const int rows_per_b = topk_idx_out ? D.N : R;
     const int n_base = topk_idx_out ? 0 : n0;
+    const int H = D.IH;   // index rows per token in the indexer and top-k
     if (P.decode) {
-      e = dsa::launch_indexer_scan(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
+      e = dsa::launch_indexer_scan(D, q_idx, k_idx, n0 * H, R * H, ncols, scores, P.ld, false,
+                                   route, s);
       if (e == hipSuccess)
-        e = dsa::launch_topk_split(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route,
-                                   w + P.tk_off, s);
+        e = dsa::launch_topk_split(D, scores, P.ld, n0 * H, R * H, idx, rows_per_b * H,
+                                   n_base * H, route, w + P.tk_off, s);
     } else {
-      e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0, R, ncols, scores, P.ld, false, route, s);
+      e = dsa::launch_indexer_tiles(D, q_idx, k_idx, n0 * H, R * H, ncols, scores, P.ld, false,
+                                    route, s);
       if (e == hipSuccess)
-        e = dsa::launch_topk_rows(D, scores, P.ld, n0, R, idx, rows_per_b, n_base, route, s);
+        e = dsa::launch_topk_rows(D, scores, P.ld, n0 * H, R * H, idx, rows_per_b * H,
+                                  n_base * H, route, s);
     }
     if (e != hipSuccess) break;
     dsa::AttnArgs a{};
@@ -464,7 +485,7 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
     a.n0 = n0; a.R = R;
     a.splits_sparse = P.splits_sparse;
     a.splits_dense = P.splits_dense;
-    if (!P.decode && dsa::mfma_attention_supported(D)) {
+    if (D.N > kDecodeRows && dsa::mfma_attention_supported(D)) {
       a.sparse_heads_per_item = sparse_heads_per_item(D);
       e = dsa::launch_attention_mfma(D, a, s);
     } else {

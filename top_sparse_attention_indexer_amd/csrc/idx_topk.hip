@@ -59,6 +59,7 @@ struct FilterArgs {
   int n0, R;          // query rows [n0, n0 + R) of each sequence
   int cap, nkc;       // list capacity; key chunks of the longest row
   long long B_rows;   // B * R
+  int rpt;            // virtual rows per token (indexer heads)
 };
 
 // Scores of 16 keys (rows of the A operand: key j0 + i for lane i of each
@@ -96,9 +97,9 @@ __global__ __launch_bounds__(FT) void k_idx_tau(FilterArgs a) {
   if (r0 >= a.R) return;                       // wave-uniform; no block barrier below
   const int r = r0 + i;
   const bool rv = r < a.R;
-  const int p = a.L - a.N + a.n0 + (rv ? r : r0);   // this column's last visible key
+  const int p = a.L - a.N + (a.n0 + (rv ? r : r0)) / a.rpt;   // this column's last visible key
   const int vis = p + 1;
-  const int p_hi = a.L - a.N + a.n0 + min(a.R - 1, r0 + 15);
+  const int p_hi = a.L - a.N + (a.n0 + min(a.R - 1, r0 + 15)) / a.rpt;
   const bool need = rv && vis > a.K && any_sparse(a.route, b, a.Hq);
   if (p_hi + 1 <= a.K || !any_sparse(a.route, b, a.Hq)) {
     if (rv && q == 0) a.tau[(size_t)b * a.R + r] = -INFINITY;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(FT) void k_idx_tau(FilterArgs a) {
   }
   bf16x8 qb[T];
   {
-    const bf16_bits* qr = a.q_idx + ((size_t)b * a.N + a.n0 + (rv ? r : r0)) * DIDX;
+    const bf16_bits* qr = a.q_idx + ((size_t)b * a.N * a.rpt + a.n0 + (rv ? r : r0)) * DIDX;
 #pragma unroll
     for (int t = 0; t < T; ++t)
       qb[t] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + t * 32 + q * 8));
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
   const int q = lane >> 4, i = lane & 15;
   const int rb0 = blockIdx.x * kRowsPerWg;
   // block-uniform exits: the block's last row bounds the keys it scans
-  const int p_blk = a.L - a.N + a.n0 + min(a.R - 1, rb0 + kRowsPerWg - 1);
+  const int p_blk = a.L - a.N + (a.n0 + min(a.R - 1, rb0 + kRowsPerWg - 1)) / a.rpt;
   const int j_lo = kc * KC;
   if (j_lo > p_blk || p_blk + 1 <= a.K || !any_sparse(a.route, b, a.Hq)) return;
   const int j_hi = min(j_lo + KC, p_blk + 1);   // keys [j_lo, j_hi) of this tile
@@ -224,12 +225,12 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
   const int r = r0 + i;
   const bool rv = r < a.R;
   const size_t row = (size_t)b * a.R + (rv ? r : 0);
-  const int p = a.L - a.N + a.n0 + (rv ? r : 0);
+  const int p = a.L - a.N + (a.n0 + (rv ? r : 0)) / a.rpt;
   const bool need = rv && p + 1 > a.K && j_lo <= p;
   const float tau = need ? a.tau[row] : INFINITY;
   bf16x8 qb[T];
   {
-    const bf16_bits* qr = a.q_idx + ((size_t)b * a.N + a.n0 + (rv ? r : 0)) * DIDX;
+    const bf16_bits* qr = a.q_idx + ((size_t)b * a.N * a.rpt + a.n0 + (rv ? r : 0)) * DIDX;
 #pragma unroll
     for (int t = 0; t < T; ++t)
       qb[t] = as_bf16x8(rv ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();                               // the whole tile has landed
   // this wave's rows see keys up to p_w
-  const int p_w = a.L - a.N + a.n0 + min(a.R - 1, r0 + 15);
+  const int p_w = a.L - a.N + (a.n0 + min(a.R - 1, r0 + 15)) / a.rpt;
   if (r0 < a.R && j_lo <= p_w) {
     for (int j0 = j_lo; j0 < j_hi && j0 <= p_w; j0 += 16) {
       const int u = (j0 - j_lo) >> 4;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(FT) void k_idx_offsets(FilterArgs a) {
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (long long)a.B_rows) return;
   const int b = (int)(row / a.R), r = (int)(row - (long long)b * a.R);
-  const int p = a.L - a.N + a.n0 + r;
+  const int p = a.L - a.N + (a.n0 + r) / a.rpt;
   if (p + 1 <= a.K) return;
   const int nk = p / KC + 1;
   int32_t* cc = a.ccnt + (size_t)row * a.nkc;
@@ -329,6 +330,7 @@ struct SelectArgs {
   int32_t* topk; int idx_rows_per_b, idx_n_base;
   int N, L, K, Hq;
   int n0, R, cap;
+  int rpt;            // virtual rows per token (indexer heads)
 };
 
 constexpr int kCandLds = 6144;   // list entries held in LDS (cap must not exceed it)
@@ -345,7 +347,7 @@ __device__ void select_stream(const SelectArgs& a, int b, int n, int vis, int32_
   constexpr int NW = CT / 64;
   bf16x8 qb[T];
   {
-    const bf16_bits* qr = a.q_idx + ((size_t)b * a.N + n) * DIDX;
+    const bf16_bits* qr = a.q_idx + ((size_t)b * a.N * a.rpt + n) * DIDX;
 #pragma unroll
     for (int t = 0; t < T; ++t)
       qb[t] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + t * 32 + q * 8));
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(CT) void k_topk_cands(SelectArgs a) {
   const int r = blockIdx.x, b = blockIdx.y;
   const int n = a.n0 + r;
   int32_t* o = a.topk + ((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.K;
-  const int vis = a.L - a.N + n + 1;
+  const int vis = a.L - a.N + n / a.rpt + 1;
   if (!any_sparse(a.route, b, a.Hq)) {
     for (int x = threadIdx.x; x < a.K; x += CT) o[x] = -1;
     return;
@@ -513,13 +515,15 @@ hipError_t launch_idx_topk(const Dims& D, const void* q_idx, const void* k_idx, 
   f.ccnt = (int32_t*)w;
   f.N = D.N; f.L = D.L; f.K = D.K; f.Hq = D.Hq; f.n0 = n0; f.R = R;
   f.B_rows = (long long)rows;
+  f.rpt = D.IH;
   SelectArgs sa{};
   sa.q_idx = f.q_idx; sa.k_idx = f.k_idx; sa.route = route;
   sa.cand = f.cand; sa.count = f.count;
   sa.topk = topk; sa.idx_rows_per_b = idx_rows_per_b; sa.idx_n_base = idx_n_base;
   sa.N = D.N; sa.L = D.L; sa.K = D.K; sa.Hq = D.Hq; sa.n0 = n0; sa.R = R; sa.cap = f.cap;
+  sa.rpt = D.IH;
   const int rb = (R + kRowsPerWg - 1) / kRowsPerWg;
-  const int nk_used = (D.L - D.N + n0 + R - 1) / KC + 1;   // chunks the last row sees
+  const int nk_used = (D.L - D.N + (n0 + R - 1) / D.IH) / KC + 1;   // chunks the last row sees
   const dim3 gt(rb, D.B), gscan(rb, nk_used, D.B), gs(R, D.B);
   const dim3 goff((unsigned)((rows + 3) / 4));
   {

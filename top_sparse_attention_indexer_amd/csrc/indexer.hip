@@ -23,13 +23,13 @@ template <typename TI>
 __global__ __launch_bounds__(256) void k_indexer_tiles(
     const TI* __restrict__ q_idx, const TI* __restrict__ k_idx, int N, int L, int D,
     int n0, int R, int ncols, float* __restrict__ out, size_t ld, int write_masked,
-    const uint8_t* __restrict__ route, int Hq) {
+    const uint8_t* __restrict__ route, int Hq, int rpt) {
   const int b = blockIdx.z;
   const int r0 = blockIdx.y * 64;
   const int j0 = blockIdx.x * 64;
   if (!seq_has_sparse(route, b, Hq)) return;
   const int rows_here = min(64, R - r0);
-  const int p_last = L - N + n0 + r0 + rows_here - 1;
+  const int p_last = L - N + (n0 + r0 + rows_here - 1) / rpt;
   const bool tile_masked = j0 > p_last;
   if (tile_masked && !write_masked) return;
 
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void k_indexer_tiles(
         const int rr = e >> 5, cc = e & 31;
         const int rq = r0 + rr, jk = j0 + rr;
         float qv = 0.f, kv = 0.f;
-        if (rq < R && c0 + cc < D) qv = ld_f(q_idx, ((size_t)b * N + n0 + rq) * D + c0 + cc);
+        if (rq < R && c0 + cc < D) qv = ld_f(q_idx, ((size_t)b * N * rpt + n0 + rq) * D + c0 + cc);
         if (jk < L && c0 + cc < D) kv = ld_f(k_idx, ((size_t)b * L + jk) * D + c0 + cc);
         qs[rr][cc] = qv;
         ks[rr][cc] = kv;
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_indexer_tiles(
   for (int i = 0; i < 4; ++i) {
     const int r = r0 + ty * 4 + i;
     if (r >= R) continue;
-    const int p = L - N + n0 + r;
+    const int p = L - N + (n0 + r) / rpt;
     float* orow = out + ((size_t)b * R + r) * ld;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -96,7 +96,7 @@ template <int DIDX>
 __global__ __launch_bounds__(256) void k_indexer_mfma(
     const bf16_bits* __restrict__ q_idx, const bf16_bits* __restrict__ k_idx, int N, int L,
     int n0, int R, int ncols, float* __restrict__ out, size_t ld, int write_masked,
-    const uint8_t* __restrict__ route, int Hq) {
+    const uint8_t* __restrict__ route, int Hq, int rpt) {
   constexpr int T = DIDX / 32;
   constexpr int UB = T <= 2 ? 8 : 4;   // key blocks whose loads are in flight together
   const int b = blockIdx.z;
@@ -104,16 +104,16 @@ __global__ __launch_bounds__(256) void k_indexer_mfma(
   const int j0 = blockIdx.x * 128;
   if (!seq_has_sparse(route, b, Hq)) return;
   const int rows_here = min(64, R - r0);
-  const int p_last = L - N + n0 + r0 + rows_here - 1;
+  const int p_last = L - N + (n0 + r0 + rows_here - 1) / rpt;
   if (j0 > p_last && !write_masked) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, i = lane & 15;
   const int r = r0 + w * 16 + i;      // this lane's query row
   const bool rv = r < R;
-  const int p = L - N + n0 + r;
+  const int p = L - N + (n0 + r) / rpt;
   bf16x8 qb[T];
   {
-    const bf16_bits* qr = q_idx + ((size_t)b * N + n0 + (rv ? r : 0)) * DIDX;
+    const bf16_bits* qr = q_idx + ((size_t)b * N * rpt + n0 + (rv ? r : 0)) * DIDX;
 #pragma unroll
     for (int t = 0; t < T; ++t)
       qb[t] = as_bf16x8(rv ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
@@ -166,16 +166,16 @@ template <typename TI, int RM>
 __global__ __launch_bounds__(256) void k_indexer_scan(
     const TI* __restrict__ q_idx, const TI* __restrict__ k_idx, int N, int L, int D,
     int n0, int R, int ncols, float* __restrict__ out, size_t ld, int write_masked,
-    const uint8_t* __restrict__ route, int Hq) {
+    const uint8_t* __restrict__ route, int Hq, int rpt) {
   const int b = blockIdx.y;
   if (!seq_has_sparse(route, b, Hq)) return;
   __shared__ float qs[RM][128];
   for (int e = threadIdx.x; e < R * D; e += 256) {
     const int r = e / D, c = e - r * D;
-    qs[r][c] = ld_f(q_idx, ((size_t)b * N + n0 + r) * D + c);
+    qs[r][c] = ld_f(q_idx, ((size_t)b * N * rpt + n0 + r) * D + c);
   }
   __syncthreads();
-  const int p_max = L - N + n0 + R - 1;
+  const int p_max = L - N + (n0 + R - 1) / rpt;
   for (int j = blockIdx.x * 256 + threadIdx.x; j < ncols; j += gridDim.x * 256) {
     float acc[RM];
 #pragma unroll
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void k_indexer_scan(
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
       if (r >= R) break;
-      const int p = L - N + n0 + r;
+      const int p = L - N + (n0 + r) / rpt;
       float* orow = out + ((size_t)b * R + r) * ld;
       if (j <= p) orow[j] = acc[r];
       else if (write_masked) orow[j] = -INFINITY;
@@ -209,7 +209,7 @@ hipError_t scan_dispatch(const Dims& D, const TI* qi, const TI* ki, int n0, int 
   dim3 grid(blocks, D.B);
 #define DSA_SCAN(RM)                                                                          \
   hipLaunchKernelGGL((k_indexer_scan<TI, RM>), grid, dim3(256), 0, s, qi, ki, D.N, D.L, D.didx, \
-                     n0, R, ncols, out, ld, (int)wm, route, D.Hq)
+                     n0, R, ncols, out, ld, (int)wm, route, D.Hq, D.IH)
   if (R <= 1) DSA_SCAN(1);
   else if (R <= 2) DSA_SCAN(2);
   else if (R <= 4) DSA_SCAN(4);
@@ -230,7 +230,7 @@ hipError_t launch_indexer_tiles(const Dims& D, const void* q_idx, const void* k_
 #define DSA_IDX_MFMA(DI)                                                                       \
   hipLaunchKernelGGL(k_indexer_mfma<DI>, g, dim3(256), 0, s, (const bf16_bits*)q_idx,           \
                      (const bf16_bits*)k_idx, D.N, D.L, n0, R, ncols, out, ld, (int)write_masked, \
-                     route, D.Hq)
+                     route, D.Hq, D.IH)
     if (D.didx == 32) DSA_IDX_MFMA(32);
     else if (D.didx == 64) DSA_IDX_MFMA(64);
     else DSA_IDX_MFMA(128);
@@ -241,11 +241,11 @@ hipError_t launch_indexer_tiles(const Dims& D, const void* q_idx, const void* k_
   if (D.idx_bf16)
     hipLaunchKernelGGL(k_indexer_tiles<bf16_bits>, grid, dim3(256), 0, s, (const bf16_bits*)q_idx,
                        (const bf16_bits*)k_idx, D.N, D.L, D.didx, n0, R, ncols, out, ld,
-                       (int)write_masked, route, D.Hq);
+                       (int)write_masked, route, D.Hq, D.IH);
   else
     hipLaunchKernelGGL(k_indexer_tiles<float>, grid, dim3(256), 0, s, (const float*)q_idx,
                        (const float*)k_idx, D.N, D.L, D.didx, n0, R, ncols, out, ld,
-                       (int)write_masked, route, D.Hq);
+                       (int)write_masked, route, D.Hq, D.IH);
   return hipGetLastError();
 }
 

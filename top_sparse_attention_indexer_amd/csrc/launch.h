@@ -13,6 +13,12 @@ struct Dims {
   int B, N, L, Hq, Hkv, d, didx, K;
   bool qkv_bf16, idx_bf16;
   float scale;  // resolved softmax scale (> 0)
+  // indexer heads: 1 = one selected set per token shared by every head; IH
+  // > 1 = one set per (token, indexer head), query head h using set
+  // h / (Hq / IH).  The indexer and top-k stages then work on IH "virtual
+  // rows" per token: q_idx row and index row n * IH + i, visible prefix that
+  // of token n.  Their n0 / R / index-row arguments count virtual rows.
+  int IH = 1;
 };
 
 // ---- indexer ---------------------------------------------------------------

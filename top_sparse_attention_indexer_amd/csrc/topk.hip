@@ -102,11 +102,11 @@ __global__ __launch_bounds__(RT) void k_topk_rows(const float* __restrict__ scor
                                                   int N, int L, int K, int n0, int R,
                                                   int32_t* __restrict__ topk, int idx_rows_per_b,
                                                   int idx_n_base, const uint8_t* __restrict__ route,
-                                                  int Hq) {
+                                                  int Hq, int rpt) {
   const int r = blockIdx.x, b = blockIdx.y;
   const int n = n0 + r;
   int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
-  const int vis = L - N + n + 1;
+  const int vis = L - N + n / rpt + 1;
   if (!row_has_sparse(route, b, Hq)) {
     for (int i = threadIdx.x; i < K; i += RT) o[i] = -1;
     return;
@@ -141,11 +141,11 @@ __global__ __launch_bounds__(CT) void k_topk_cand(const float* __restrict__ scor
                                                   int N, int L, int K, int n0, int R,
                                                   int32_t* __restrict__ topk, int idx_rows_per_b,
                                                   int idx_n_base, const uint8_t* __restrict__ route,
-                                                  int Hq) {
+                                                  int Hq, int rpt) {
   const int r = blockIdx.x, b = blockIdx.y;
   const int n = n0 + r;
   int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
-  const int vis = L - N + n + 1;
+  const int vis = L - N + n / rpt + 1;
   if (!row_has_sparse(route, b, Hq)) {
     for (int i = threadIdx.x; i < K; i += CT) o[i] = -1;
     return;
@@ -350,10 +350,10 @@ template <int LV>
 __global__ __launch_bounds__(ST) void k_split_hist(const float* __restrict__ scores, size_t ld,
                                                    int N, int L, int K, int n0, int R,
                                                    SplitWs ws, const uint8_t* __restrict__ route,
-                                                   int Hq) {
+                                                   int Hq, int rpt) {
   const int c = blockIdx.x, row = blockIdx.y;  // row = b * R + r
   const int b = row / R, r = row - b * R;
-  const int vis = L - N + n0 + r + 1;
+  const int vis = L - N + (n0 + r) / rpt + 1;
   if (vis <= K || !row_has_sparse(route, b, Hq)) return;
   const int j0 = c * SCH, j1 = min(vis, j0 + SCH);
   if (j0 >= j1) return;
@@ -382,10 +382,10 @@ __global__ __launch_bounds__(ST) void k_split_hist(const float* __restrict__ sco
 __global__ __launch_bounds__(ST) void k_split_count(const float* __restrict__ scores, size_t ld,
                                                     int N, int L, int K, int n0, int R,
                                                     SplitWs ws, const uint8_t* __restrict__ route,
-                                                    int Hq) {
+                                                    int Hq, int rpt) {
   const int c = blockIdx.x, row = blockIdx.y;
   const int b = row / R, r = row - b * R;
-  const int vis = L - N + n0 + r + 1;
+  const int vis = L - N + (n0 + r) / rpt + 1;
   if (vis <= K || !row_has_sparse(route, b, Hq)) return;
   const int j0 = c * SCH, j1 = min(vis, j0 + SCH);
   __shared__ uint32_t lhist[2048];
@@ -419,11 +419,12 @@ __global__ __launch_bounds__(ST) void k_split_compact(const float* __restrict__ 
                                                       int N, int L, int K, int n0, int R,
                                                       SplitWs ws, int32_t* __restrict__ topk,
                                                       int idx_rows_per_b, int idx_n_base,
-                                                      const uint8_t* __restrict__ route, int Hq) {
+                                                      const uint8_t* __restrict__ route, int Hq,
+                                                      int rpt) {
   const int c = blockIdx.x, row = blockIdx.y;
   const int b = row / R, r = row - b * R;
   const int n = n0 + r;
-  const int vis = L - N + n + 1;
+  const int vis = L - N + n / rpt + 1;
   int32_t* o = topk + ((size_t)b * idx_rows_per_b + (n - idx_n_base)) * K;
   if (!row_has_sparse(route, b, Hq)) {
     if (c == 0)
@@ -494,18 +495,18 @@ hipError_t launch_topk_rows(const Dims& D, const float* scores, size_t ld, int n
   if (D.B == 0 || R == 0) return hipSuccess;
   // rows up to kMaxWords * 32 positions: one read of the row (candidate
   // list in LDS); longer rows: the multi-pass kernel
-  const long long vmax = (long long)D.L - D.N + n0 + R;
+  const long long vmax = (long long)D.L - D.N + (n0 + R - 1) / D.IH + 1;
   const dim3 grid(R, D.B);
   ProfScope ps(s, kStageTopk);
   if (vmax <= 32768)
     hipLaunchKernelGGL((k_topk_cand<512, 6144>), grid, dim3(512), 0, s, scores, ld, D.N, D.L, D.K,
-                       n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq);
+                       n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq, D.IH);
   else if (vmax <= (long long)kMaxWords * 32)
     hipLaunchKernelGGL((k_topk_cand<1024, 8192>), grid, dim3(1024), 0, s, scores, ld, D.N, D.L,
-                       D.K, n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq);
+                       D.K, n0, R, topk, idx_rows_per_b, idx_n_base, route, D.Hq, D.IH);
   else
     hipLaunchKernelGGL(k_topk_rows, grid, dim3(RT), 0, s, scores, ld, D.N, D.L, D.K, n0, R, topk,
-                       idx_rows_per_b, idx_n_base, route, D.Hq);
+                       idx_rows_per_b, idx_n_base, route, D.Hq, D.IH);
   return hipGetLastError();
 }
 
@@ -530,15 +531,15 @@ hipError_t launch_topk_split(const Dims& D, const float* scores, size_t ld, int 
   if (e != hipSuccess) return e;
   const dim3 grid(ws.nchunks, rows);
   hipLaunchKernelGGL(k_split_hist<0>, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
-                     route, D.Hq);
+                     route, D.Hq, D.IH);
   hipLaunchKernelGGL(k_split_hist<1>, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
-                     route, D.Hq);
+                     route, D.Hq, D.IH);
   hipLaunchKernelGGL(k_split_hist<2>, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
-                     route, D.Hq);
+                     route, D.Hq, D.IH);
   hipLaunchKernelGGL(k_split_count, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
-                     route, D.Hq);
+                     route, D.Hq, D.IH);
   hipLaunchKernelGGL(k_split_compact, grid, dim3(ST), 0, s, scores, ld, D.N, D.L, D.K, n0, R, ws,
-                     topk, idx_rows_per_b, idx_n_base, route, D.Hq);
+                     topk, idx_rows_per_b, idx_n_base, route, D.Hq, D.IH);
   return hipGetLastError();
 }
 

@@ -85,10 +85,15 @@ WORKLOADS: Dict[str, Workload] = {
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    # in place on 32-bit patterns: for every finite or infinite value the
+    # rounding increment cannot carry past bit 31
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    u += r
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
