@@ -39,13 +39,21 @@ the design notes of the repository):
   * softmax scale 1/sqrt(d) unless given; query head h reads KV head
     h // (Hq / Hkv);
   * gate given post-sigmoid, blended as g*a + (1-g)*y2 for both routes;
-  * route[b, h] = 1 means top-k sparse, 0 means full causal attention.
+  * route[b, h] = 1 means top-k sparse, 0 means full causal attention;
+  * the route producer ([EA] §2.2): the router's input is the mean over the
+    tokens of the call (positions L - N .. L - 1) of their keys, one vector
+    of Hkv * d; the 2-layer MLP is linear, ReLU, linear with two logits per
+    query head (column 0 full, column 1 sparse); inference takes the hard
+    decision of the Gumbel-Softmax/straight-through training, the larger
+    logit, a tie going to full attention.
 
 Pins (tests, CPU): closed forms for the indexer, brute force over all
 subsets for tiny top-k rows plus the closed-form orderings, the special case
 K >= visible against torch's scaled_dot_product_attention in float64 (and a
 boolean-mask SDPA for the sparse case), hand-derived worked examples under
-tests/golden, and the exact gate end points.  Nothing here is unpinned.
+tests/golden, the exact gate end points, and for the router a hand-derived
+example (ReLU cut, bias, tie), invariances and torch's linear layers in
+float64.  Nothing here is unpinned.
 """
 from __future__ import annotations
 
@@ -218,3 +226,43 @@ def dense_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
         p /= p.sum(axis=1, keepdims=True)
         out[:, h] = p @ vh
     return out
+
+
+def route_heads(k_current: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray,
+                b2: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-head route of one sequence from the attention router, in float64.
+
+    [EA] §2.2: a light router in every layer takes the current key hidden
+    states, is a two-layer MLP and decides per attention head between full
+    and sparse attention; it is trained through Gumbel-Softmax with a
+    straight-through estimator, so at inference the decision is hard: the
+    option with the larger logit.
+
+    k_current [n, Hkv, d]: keys of the tokens of the call.  w1 [Hkv*d, Hr],
+    b1 [Hr], w2 [Hr, Hq, 2], b2 [Hq, 2]; column 0 of the last axis is full
+    attention, column 1 sparse.  Returns (logits [Hq, 2], route [Hq] uint8
+    with 1 = sparse); a tie keeps full attention.
+    """
+    n = k_current.shape[0]
+    x = k_current.reshape(n, -1).astype(np.float64).sum(axis=0) / n   # mean key vector
+    hidden = x @ w1.astype(np.float64) + b1.astype(np.float64)
+    hidden = np.where(hidden > 0.0, hidden, 0.0)                      # ReLU
+    h_r, h_q = w2.shape[0], w2.shape[1]
+    logits = (hidden @ w2.reshape(h_r, h_q * 2).astype(np.float64)).reshape(h_q, 2)
+    logits = logits + b2.astype(np.float64)
+    route = (logits[:, 1] > logits[:, 0]).astype(np.uint8)
+    return logits, route
+
+
+def route_batch(params, k: np.ndarray, router: Dict[str, np.ndarray]
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """route_heads for every sequence: the current tokens are the last n_q
+    positions of each sequence's keys.  Returns logits [B, Hq, 2] and
+    route [B, Hq]."""
+    L, N = params.kv_len, params.n_q
+    logits = np.zeros((params.batch, params.h_q, 2), dtype=np.float64)
+    route = np.zeros((params.batch, params.h_q), dtype=np.uint8)
+    for b in range(params.batch):
+        logits[b], route[b] = route_heads(k[b, L - N:L], router["w1"], router["b1"],
+                                          router["w2"], router["b2"])
+    return logits, route

@@ -361,3 +361,84 @@ def test_per_head_with_equal_queries_is_the_shared_selection():
     oh, ih = O.forward(wh, xh)
     assert np.array_equal(ih, np.repeat(i1[:, :, None, :], 4, axis=2))
     assert np.array_equal(oh, o1)
+
+
+# --------------------------------------------------------------------------- route producer
+def test_router_golden():
+    """Hand-derived example: mean pooling, a unit cut by the ReLU, the bias,
+    and a tie that keeps full attention ([EA] §2.2)."""
+    g = _golden()["router"]
+    k = np.array(g["k_current"], dtype=np.float64)
+    logits, route = O.route_heads(k, np.array(g["w1"], float), np.array(g["b1"], float),
+                                  np.array(g["w2"], float), np.array(g["b2"], float))
+    np.testing.assert_array_equal(logits, np.array(g["logits"], float))
+    np.testing.assert_array_equal(route, np.array(g["route"], np.uint8))
+
+
+def _router_case(seed=3, n=5, h_kv=2, d=8, hidden=16, h_q=6):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n, h_kv, d))
+    r = {"w1": rng.standard_normal((h_kv * d, hidden)), "b1": rng.standard_normal(hidden),
+         "w2": rng.standard_normal((hidden, h_q, 2)), "b2": rng.standard_normal((h_q, 2))}
+    return k, r
+
+
+def test_router_matches_torch_linear_layers():
+    """The same MLP built from torch's linear layers in float64 on the mean key."""
+    k, r = _router_case()
+    logits, route = O.route_heads(k, r["w1"], r["b1"], r["w2"], r["b2"])
+    x = torch.from_numpy(k.reshape(k.shape[0], -1)).mean(dim=0)
+    hid = torch.nn.functional.relu(torch.nn.functional.linear(
+        x, torch.from_numpy(r["w1"]).T, torch.from_numpy(r["b1"])))
+    want = torch.nn.functional.linear(hid, torch.from_numpy(r["w2"].reshape(16, -1)).T,
+                                      torch.from_numpy(r["b2"].reshape(-1))).reshape(-1, 2)
+    np.testing.assert_allclose(logits, want.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(route, torch.argmax(want, dim=1).numpy().astype(np.uint8))
+
+
+def test_router_invariances():
+    k, r = _router_case(seed=4)
+    logits, route = O.route_heads(k, r["w1"], r["b1"], r["w2"], r["b2"])
+    # the order of the current tokens does not matter (pooling), their values do
+    l2, r2 = O.route_heads(k[::-1], r["w1"], r["b1"], r["w2"], r["b2"])
+    np.testing.assert_allclose(l2, logits, rtol=1e-12, atol=1e-12)
+    l3, _ = O.route_heads(k[:-1], r["w1"], r["b1"], r["w2"], r["b2"])
+    assert not np.allclose(l3, logits)
+    # swapping the full and sparse columns flips every decision
+    l4, r4 = O.route_heads(k, r["w1"], r["b1"], r["w2"][:, :, ::-1], r["b2"][:, ::-1])
+    assert np.all(logits[:, 0] != logits[:, 1])
+    np.testing.assert_array_equal(r4, 1 - route)
+    # a positive scale of the output layer keeps every decision
+    _, r5 = O.route_heads(k, r["w1"], r["b1"], r["w2"] * 3.0, r["b2"] * 3.0)
+    np.testing.assert_array_equal(r5, route)
+    # a large negative first-layer bias silences every unit: the decision is b2's
+    _, r6 = O.route_heads(k, r["w1"], r["b1"] - 1e6, r["w2"], r["b2"])
+    np.testing.assert_array_equal(r6, (r["b2"][:, 1] > r["b2"][:, 0]).astype(np.uint8))
+
+
+def test_router_reads_only_the_current_tokens():
+    """route_batch pools keys L - N .. L - 1 of each sequence: changing the
+    earlier context leaves the route unchanged, changing a current key does not."""
+    w = synth.Workload("r", 2, 3, 10, 4, 2, 8, 16, 4, "fp32", "fp32", (-4, 4), seed=9)
+    x = synth.make_inputs(w)
+    r = synth.make_router(w, hidden=16)
+    logits, route = O.route_batch(w, x["k"], r)
+    k2 = x["k"].copy()
+    k2[:, :7] = 100.0
+    l2, _ = O.route_batch(w, k2, r)
+    np.testing.assert_array_equal(l2, logits)
+    k2[1, 9, 0, 0] += 1.0
+    l3, _ = O.route_batch(w, k2, r)
+    np.testing.assert_array_equal(l3[0], logits[0])
+    assert not np.allclose(l3[1], logits[1])
+
+
+def test_router_size_matches_the_stated_parameter_count():
+    """[EA] §2.2 puts the router near 0.27 M parameters per layer: with the
+    keys of 8 KV heads of 128 dims, 256 hidden units and two logits for each
+    of 32 query heads the MLP has 0.279 M."""
+    w = synth.WORKLOADS["elastic_prefill_64k"]
+    r = synth.make_router(w)
+    count = sum(v.size for v in r.values())
+    assert count == 1024 * 256 + 256 + 256 * 64 + 64
+    assert abs(count - 0.27e6) / 0.27e6 < 0.05

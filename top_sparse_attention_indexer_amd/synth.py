@@ -32,6 +32,7 @@ representable in the workload's storage dtype; ``to_bf16_bits`` gives the
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -162,6 +163,32 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
             out["route"] = (rng["route"].random(size=(B, w.h_q))
                             < w.route_sparse_p).astype(np.uint8)
     return out
+
+
+def make_router(w: Workload, hidden: int = 256, sparse_share: float = 0.7,
+                seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Seeded random weights of the two-layer attention router (no trained
+    weights exist here), float32: w1 [Hkv*d, hidden], b1 [hidden],
+    w2 [hidden, Hq, 2], b2 [Hq, 2] (column 0 full, column 1 sparse).
+
+    Scales: the mean of n iid N(0, 1) keys has per-component variance 1/n,
+    so w1 ~ N(0, n / (Hkv*d)) gives pre-activations of unit variance;
+    b1 ~ N(0, 0.1^2); w2 ~ N(0, 1 / hidden) gives logit differences of
+    about unit variance; b2 shifts the sparse column by the normal quantile
+    of ``sparse_share``, so that about that share of heads goes sparse.
+    """
+    import statistics
+    seed = w.seed + 500 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    c = w.h_kv * w.head_dim
+    n = max(1, w.n_q)
+    w1 = rng.standard_normal((c, hidden)) * math.sqrt(n / c)
+    b1 = rng.standard_normal(hidden) * 0.1
+    w2 = rng.standard_normal((hidden, w.h_q, 2)) / math.sqrt(hidden)
+    b2 = np.zeros((w.h_q, 2))
+    b2[:, 1] = statistics.NormalDist().inv_cdf(sparse_share)
+    return {k: v.astype(np.float32) for k, v in
+            (("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2))}
 
 
 def sample_rows(w: Workload, count: int, seed: int = 7) -> np.ndarray:
