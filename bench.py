@@ -133,6 +133,12 @@ def stage_rooflines(w, m, stages, steps):
         out["merge"] = {"ms": per["merge"][0], "launches": per["merge"][1]}
     if "prep" in per:
         out["prep"] = {"ms": per["prep"][0], "launches": per["prep"][1]}
+    if "route" in per and "route_bytes" in m:
+        t = per["route"][0] * 1e-3
+        a = m["route_bytes"] / t / 1e9
+        out["route"] = {"ms": per["route"][0], "launches": per["route"][1], "bound": "hbm",
+                        "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": a / HBM_PEAK_GBS}
     if "decode" in per:
         t = per["decode"][0] * 1e-3
         a = m["bytes"] / t / 1e9
@@ -217,29 +223,80 @@ class Runner:
                                  self.stream)
 
 
-def timed(runners, steps, warmup, profile=True):
+class RoutedRunner:
+    """The forward with the route made on the device by the two-layer router
+    (seeded random weights): dsa_fused_forward_routed, or the router alone."""
+
+    def __init__(self, base, hidden=256, router_only=False):
+        import torch
+        from top_sparse_attention_indexer_amd import synth
+        B, w = base.B, base.w
+        self.B, self.w, self.base, self.router_only = B, w, base, router_only
+        self.weights = {k: torch.from_numpy(v).cuda()
+                        for k, v in synth.make_router(w, hidden=hidden).items()}
+        self.r = B.router(self.weights["w1"], self.weights["b1"], self.weights["w2"],
+                          self.weights["b2"])
+        self.hidden = hidden
+        self.route = torch.empty((w.batch, w.h_q), dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(max(1, B.dsa_route_workspace_size(base.p, self.r)),
+                              dtype=torch.uint8, device="cuda")
+        self.stream = base.stream
+
+    def step(self):
+        b, d = self.base, self.base.dev
+        if self.router_only:
+            self.B.dsa_route_heads(b.p, self.r, d["k"], self.route, None, self.ws, self.stream)
+        else:
+            self.B.dsa_fused_forward_routed(b.p, self.r, d["q_idx"], d["k_idx"], d["q"], d["k"],
+                                            d["v"], d["gate"], d["y2"], self.route, b.out,
+                                            b.idx, self.ws, self.stream)
+
+    def route_bytes(self):
+        """Keys of the call's tokens once, the router weights once."""
+        w = self.w
+        c = w.h_kv * w.head_dim
+        bq = 2 if w.qkv_dtype == "bf16" else 4
+        weights = (c * self.hidden + self.hidden + self.hidden * 2 * w.h_q + 2 * w.h_q) * 4
+        return w.batch * w.n_q * c * bq + weights
+
+
+def timed(runners, steps, warmup):
     """Warm-up, then `steps` back-to-back steps (cycling over the runners)
     between two events on the launch stream; stage timing over the same
-    region.  Returns ms per step, per-step spread and the stage sums."""
+    region.  A step that is one timed launch group (the single-launch decode,
+    the router) is timed without the per-launch events, which would add their
+    own cost to a step of tens of microseconds: its stage time is then the
+    region's time per step.  Returns ms per step, per-step spread and the
+    stage sums."""
     import torch
     B = runners[0].B
     stream = runners[0].stream
     for i in range(warmup):
         runners[i % len(runners)].step()
     torch.cuda.synchronize()
+    # launch groups per step, from one profiled step
+    B.dsa_profile_start(1 << 10)
+    runners[0].step()
+    torch.cuda.synchronize()
+    probe = {k: v for k, v in B.dsa_profile_stop()[0].items() if v[1] > 0}
+    single = len(probe) == 1 and next(iter(probe.values()))[1] == 1
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    if profile:
+    if not single:
         B.dsa_profile_start(1 << 17)
     t0.record(stream)
     for i in range(steps):
         runners[i % len(runners)].step()
     t1.record(stream)
     torch.cuda.synchronize()
-    stages = B.dsa_profile_stop()[0] if profile else {}
     ms = t0.elapsed_time(t1) / steps
+    if single:
+        stages = {next(iter(probe)): (ms * steps, steps)}
+    else:
+        stages = B.dsa_profile_stop()[0]
     for r in runners:
-        B.dsa_exec_status(r.ws, r.stream)
+        if isinstance(r, Runner):
+            B.dsa_exec_status(r.ws, r.stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(min(steps, 20))]
     for i, (a, b_) in enumerate(ev):
@@ -335,10 +392,27 @@ def main():
         "algorithmic_flops": head["algorithmic_flops"],
     }
     x_head = runners[0].x
+    others = {}
+    if not args.no_others and args.workload == HEADLINE:
+        # the route made on the device: the router alone, then the forward with it
+        for key, only in (("route_producer", True), ("routed_forward", False)):
+            progress(f"{w.name}: {key}")
+            rr = RoutedRunner(runners[0], router_only=only)
+            ms_r, spread_r, stages_r = timed([rr], args.steps if not only else 50, 3)
+            mr = dict(work_model(w, rr.route.cpu().numpy()), route_bytes=rr.route_bytes())
+            e = {"ms_per_step": ms_r, "step_ms_p10_p50_p90": spread_r,
+                 "stages": stage_rooflines(w, mr, stages_r, args.steps if not only else 50),
+                 "hidden": rr.hidden,
+                 "sparse_share": float(rr.route.float().mean().item())}
+            if not only:
+                e["value"] = w.batch * w.n_q / (ms_r / 1e3)
+                e["unit"] = "query tokens/s"
+            progress(f"{w.name}: {key} {ms_r:.4f} ms")
+            others[key] = e
+            del rr
     del runners
     torch.cuda.empty_cache()
     if not args.no_others and args.workload == HEADLINE:
-        others = {}
         for name in OTHERS:
             wo = synth.WORKLOADS[name]
             steps = 50 if wo.n_q == 1 else args.steps

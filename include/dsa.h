@@ -165,6 +165,49 @@ dsa_status dsa_fused_forward_noalloc(const dsa_problem* p, const void* q_idx,
                                      const uint8_t* route, float* out,
                                      int32_t* topk_idx_out, void* stream);
 
+/* Weights of the per-head route producer ([EA] §2.2): a two-layer router
+ * on the keys of the call's tokens.  Device pointers, fp32, row-major,
+ * 16-byte aligned, owned by the caller:
+ *   w1 [Hkv*d, hidden], b1 [hidden], w2 [hidden, Hq, 2], b2 [Hq, 2]
+ * (last axis: column 0 full attention, column 1 sparse). */
+typedef struct {
+  int32_t hidden;    /* 1 <= hidden <= 65536 */
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+} dsa_router;
+
+/* Bytes of workspace dsa_route_heads and dsa_fused_forward_routed accept for
+ * *p and *r (the larger need of the two).  Host-only; enqueues nothing. */
+dsa_status dsa_route_workspace_size(const dsa_problem* p, const dsa_router* r, size_t* bytes);
+
+/* Route producer ([EA] §2.2: the router reads the current key hidden states,
+ * is a two-layer MLP and takes one full/sparse decision per head, hard at
+ * inference).  For each sequence b:
+ *   x = mean of the key rows k[b, j, :, :] (Hkv*d values) over the call's
+ *       tokens j = L - N .. L - 1;
+ *   z = max(0, x w1 + b1) w2 + b2         ([Hq, 2], fp32 accumulation);
+ *   route[b, h] = 1 (sparse) if z[h][1] > z[h][0], else 0 (full; a tie
+ *   keeps full attention).
+ * k [B, L, Hkv, d] in qkv dtype; route [B, Hq] uint8; logits [B, Hq, 2]
+ * float32 (nullable).  The summation order is fixed, so equal inputs give
+ * equal decisions. */
+dsa_status dsa_route_heads(const dsa_problem* p, const dsa_router* r, const void* k,
+                           uint8_t* route, float* logits, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* dsa_route_heads followed on the same stream by dsa_fused_forward with
+ * route = route_out: the decision is made on the device and read there by
+ * the indexer, top-k and attention launches (no host round trip).
+ * route_out [B, Hq] receives the decision (required, 16-byte aligned). */
+dsa_status dsa_fused_forward_routed(const dsa_problem* p, const dsa_router* r,
+                                    const void* q_idx, const void* k_idx, const void* q,
+                                    const void* k, const void* v, const float* gate,
+                                    const float* y2, uint8_t* route_out, float* out,
+                                    int32_t* topk_idx_out, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Execution status of the last dsa_fused_forward on workspace `ws`:
  * synchronises `stream` (the stream that call used), then returns
  * DSA_ERR_EXEC if that call was a single-launch decode and one of its waits
@@ -187,11 +230,11 @@ void dsa_set_wait_limit(uint32_t polls);
  * stage, the summed GPU time in milliseconds and the number of launches:
  *   0 indexer scores, 1 top-k selection, 2 attention (both routes),
  *   3 merge of split/range partials, 4 single-launch decode (the whole
- *   path), 5 preparation (range offsets, work queues).
+ *   path), 5 preparation (range offsets, work queues), 6 route producer.
  * ms and launches have n_stages entries (either may be NULL); dropped
  * (nullable) receives the count of launches not timed.  Host calls; the
  * events are created by start and destroyed by stop. */
-#define DSA_PROFILE_STAGES 6
+#define DSA_PROFILE_STAGES 7
 dsa_status dsa_profile_start(int32_t max_launches);
 dsa_status dsa_profile_stop(double* ms, int32_t* launches, int32_t n_stages,
                             int64_t* dropped);

@@ -134,3 +134,41 @@ def test_exec_status_without_a_decode_launch():
     assert lib.dsa_exec_status(None, None) == B.DSA_ERR_INVALID_ARG
     assert "null" in lib.dsa_last_error().decode()
     assert lib.dsa_exec_status(FAKE, None) == B.DSA_OK
+
+
+def test_router_arguments_are_checked_before_launch():
+    lib = B.lib()
+    p = ctypes.byref(_p())
+    good = B.DsaRouter(16, FAKE, FAKE, FAKE, FAKE)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_route_workspace_size(p, ctypes.byref(good), ctypes.byref(n)) == B.DSA_OK
+    # the routed forward needs at least what the forward needs
+    assert n.value >= B.dsa_workspace_size(_p()) > 0
+    bad = [(None, "router is null"),
+           (ctypes.byref(B.DsaRouter(0, FAKE, FAKE, FAKE, FAKE)), "hidden"),
+           (ctypes.byref(B.DsaRouter(70000, FAKE, FAKE, FAKE, FAKE)), "hidden"),
+           (ctypes.byref(B.DsaRouter(16, None, FAKE, FAKE, FAKE)), "w1"),
+           (ctypes.byref(B.DsaRouter(16, FAKE, FAKE, MISALIGNED, FAKE)), "w2")]
+    for r, msg in bad:
+        assert lib.dsa_route_workspace_size(p, r, ctypes.byref(n)) == B.DSA_ERR_INVALID_ARG
+        assert msg in lib.dsa_last_error().decode()
+        assert lib.dsa_route_heads(p, r, FAKE, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    g = ctypes.byref(good)
+    assert lib.dsa_route_heads(p, g, None, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_route_heads(p, g, FAKE, None, None, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_route_heads(p, g, FAKE, FAKE, MISALIGNED, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_route_heads(p, g, FAKE, FAKE, None, FAKE, 16, None) == B.DSA_ERR_WORKSPACE
+    # routed forward: route_out required, every forward check before the router runs
+    full = [FAKE] * 7     # q_idx, k_idx, q, k, v, gate, y2
+    assert lib.dsa_fused_forward_routed(p, g, *full, None, FAKE, None, FAKE, 1 << 30,
+                                        None) == B.DSA_ERR_INVALID_ARG
+    assert "route_out" in lib.dsa_last_error().decode()
+    a = list(full)
+    a[2] = None
+    assert lib.dsa_fused_forward_routed(p, g, *a, FAKE, FAKE, None, FAKE, 1 << 30,
+                                        None) == B.DSA_ERR_INVALID_ARG
+    assert lib.dsa_fused_forward_routed(p, g, *full, FAKE, FAKE, None, FAKE, 16,
+                                        None) == B.DSA_ERR_WORKSPACE
+    # empty problems: no-ops
+    e = ctypes.byref(B.problem(0, 4, 16, 4, 1, 64, 32, 8))
+    assert lib.dsa_route_heads(e, g, None, None, None, None, 0, None) == B.DSA_OK

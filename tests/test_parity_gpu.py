@@ -577,3 +577,98 @@ def test_per_head_entry_points(announce):
     want_out, _ = O.forward(w, x)
     err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - want_out))
     assert err <= TOL[w.qkv_dtype], f"max-abs error {err}"
+
+
+# --------------------------------------------------------------------------- route producer
+# Logits within ROUTE_TOL of the oracle (fp32 sums against float64; the router
+# weights are scaled so that logits are of order one); the decision must match
+# the oracle's wherever the oracle's two logits are more than 2 * ROUTE_TOL
+# apart, and always match the kernel's own logits (larger logit, tie -> full).
+ROUTE_TOL = 2e-3
+
+
+def _router_dev(r):
+    return {k: torch.from_numpy(v).cuda() for k, v in r.items()}
+
+
+def run_route(w, x, r, want_logits=True):
+    p = B.problem_for(w)
+    rd = _router_dev(r)
+    rr = B.router(rd["w1"], rd["b1"], rd["w2"], rd["b2"])
+    k = to_device(w, {"k": x["k"]})["k"]
+    route = torch.full((w.batch, w.h_q), 7, dtype=torch.uint8, device="cuda")
+    logits = (torch.empty((w.batch, w.h_q, 2), dtype=torch.float32, device="cuda")
+              if want_logits else None)
+    ws = torch.empty(max(1, B.dsa_route_workspace_size(p, rr)), dtype=torch.uint8, device="cuda")
+    B.dsa_route_heads(p, rr, k, route, logits, ws)
+    torch.cuda.synchronize()
+    return route.cpu().numpy(), (logits.cpu().numpy() if want_logits else None)
+
+
+def check_route(w, x, r, route, logits):
+    want_z, want_r = O.route_batch(w, x["k"], r)
+    err = np.max(np.abs(logits.astype(np.float64) - want_z))
+    assert err <= ROUTE_TOL, f"logit error {err}"
+    np.testing.assert_array_equal(route, (logits[..., 1] > logits[..., 0]).astype(np.uint8))
+    clear = np.abs(want_z[..., 1] - want_z[..., 0]) > 2 * ROUTE_TOL
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(route[clear], want_r[clear])
+    return err
+
+
+ROUTE_CASES = [
+    # 64K-token prefill of two sequences, 8 KV heads x 128 (the elastic workload)
+    ("elastic_prefill_64k", synth.WORKLOADS["elastic_prefill_64k"], 256),
+    # decode: one current token per sequence
+    ("decode_b8", synth.WORKLOADS["decode_b8_ctx128k"].replace(kv_len=4096), 256),
+    # fp32 keys, a hidden width and head count off the 64-lane grid
+    ("fp32_odd_sizes", _w(3, 333, 1000, 6, 3, 64, 32, 16, dt="fp32"), 100),
+    # rows wider than 2048 values (24 KV heads x 128), one hidden unit
+    ("wide_rows", _w(2, 50, 70, 48, 24, 128, 64, 16), 1),
+    # 192-value rows: 24 column groups, ten row lanes per workgroup
+    ("row_192", _w(1, 1000, 1000, 9, 3, 64, 32, 16), 64),
+]
+
+
+@pytest.mark.parametrize("name,w,hidden", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_heads_matches_oracle(name, w, hidden, announce):
+    x = synth.make_inputs(w, parts=("k",))
+    r = synth.make_router(w, hidden=hidden)
+    announce(f"route_heads {name} hidden={hidden} {w}")
+    route, logits = run_route(w, x, r)
+    check_route(w, x, r, route, logits)
+    # the same inputs give the same bits; logits are optional
+    route2, logits2 = run_route(w, x, r)
+    assert np.array_equal(logits2.view(np.uint32), logits.view(np.uint32))
+    route3, _ = run_route(w, x, r, want_logits=False)
+    np.testing.assert_array_equal(route3, route)
+
+
+@pytest.mark.parametrize("shape", ["prefill", "decode"])
+def test_fused_forward_routed(shape, announce):
+    """The route made on the device feeds the forward: route_out equals
+    dsa_route_heads' decision and the output is the oracle's under it."""
+    if shape == "prefill":
+        w = _w(2, 300, 5000, 8, 2, 128, 64, 256, seed=35)
+    else:
+        w = _w(4, 1, 20000, 8, 2, 128, 64, 512, seed=36)
+    x = synth.make_inputs(w)
+    r = synth.make_router(w, hidden=64)
+    route_ref, _ = run_route(w, x, r, want_logits=False)
+    assert 0 < route_ref.sum() < route_ref.size          # both routes present
+    p = B.problem_for(w)
+    rd = _router_dev(r)
+    rr = B.router(rd["w1"], rd["b1"], rd["w2"], rd["b2"])
+    dev = to_device(w, x)
+    route = torch.full((w.batch, w.h_q), 7, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.n_q, w.h_q, w.head_dim), dtype=torch.float32, device="cuda")
+    idx = torch.full(idx_shape(w), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, B.dsa_route_workspace_size(p, rr)), dtype=torch.uint8, device="cuda")
+    announce(f"fused_forward_routed {shape} {w}")
+    B.dsa_fused_forward_routed(p, rr, dev["q_idx"], dev["k_idx"], dev["q"], dev["k"], dev["v"],
+                               dev["gate"], dev["y2"], route, out, idx, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(route.cpu().numpy(), route_ref)
+    x["route"] = route_ref
+    rows = list(range(w.n_q)) if w.n_q <= 16 else synth.sample_rows(w, 16).tolist()
+    check_rows(w, x, out, idx, rows=rows)

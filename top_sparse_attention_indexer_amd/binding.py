@@ -29,6 +29,11 @@ class DsaProblem(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("idx_heads", ctypes.c_int32)]
 
 
+class DsaRouter(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
 class DsaError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -38,6 +43,7 @@ class DsaError(RuntimeError):
 _lib = None
 _vp = ctypes.c_void_p
 _PP = ctypes.POINTER(DsaProblem)
+_RP = ctypes.POINTER(DsaRouter)
 _SIGNATURES = {
     "dsa_workspace_size": (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
     "dsa_indexer_scores": (ctypes.c_int, [_PP, _vp, _vp, _vp, _vp]),
@@ -48,6 +54,10 @@ _SIGNATURES = {
                                          _vp, ctypes.c_size_t, _vp]),
     "dsa_fused_forward_noalloc": (ctypes.c_int, [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                  _vp, _vp]),
+    "dsa_route_workspace_size": (ctypes.c_int, [_PP, _RP, ctypes.POINTER(ctypes.c_size_t)]),
+    "dsa_route_heads": (ctypes.c_int, [_PP, _RP, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "dsa_fused_forward_routed": (ctypes.c_int, [_PP, _RP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "dsa_exec_status": (ctypes.c_int, [_vp, _vp]),
     "dsa_set_wait_limit": (None, [ctypes.c_uint32]),
     "dsa_profile_start": (ctypes.c_int, [ctypes.c_int32]),
@@ -161,6 +171,32 @@ def dsa_fused_forward_noalloc(p, q_idx, k_idx, q, k, v, gate, y2, route, out,
                                            _ptr(out), _ptr(topk_idx_out), _stream(stream)))
 
 
+def router(w1, b1, w2, b2) -> DsaRouter:
+    """Router weights (device float32 tensors): w1 [Hkv*d, hidden], b1 [hidden],
+    w2 [hidden, Hq, 2], b2 [Hq, 2].  The caller keeps the tensors alive."""
+    return DsaRouter(int(w1.shape[1]), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2))
+
+
+def dsa_route_workspace_size(p: DsaProblem, r: DsaRouter) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dsa_route_workspace_size(ctypes.byref(p), ctypes.byref(r), ctypes.byref(n)))
+    return n.value
+
+
+def dsa_route_heads(p, r, k, route, logits=None, ws=None, stream=None):
+    _check(lib().dsa_route_heads(ctypes.byref(p), ctypes.byref(r), _ptr(k), _ptr(route),
+                                 _ptr(logits), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def dsa_fused_forward_routed(p, r, q_idx, k_idx, q, k, v, gate, y2, route_out, out,
+                             topk_idx_out=None, ws=None, stream=None):
+    _check(lib().dsa_fused_forward_routed(ctypes.byref(p), ctypes.byref(r), _ptr(q_idx),
+                                          _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                          _ptr(y2), _ptr(route_out), _ptr(out),
+                                          _ptr(topk_idx_out), _ptr(ws), _nbytes(ws),
+                                          _stream(stream)))
+
+
 def dsa_exec_status(ws, stream=None):
     """Raises DsaError(DSA_ERR_EXEC) if the last fused forward on ``ws`` gave up."""
     _check(lib().dsa_exec_status(_ptr(ws), _stream(stream)))
@@ -170,7 +206,7 @@ def dsa_set_wait_limit(polls: int):
     lib().dsa_set_wait_limit(int(polls))
 
 
-STAGES = ("indexer", "topk", "attention", "merge", "decode", "prep")
+STAGES = ("indexer", "topk", "attention", "merge", "decode", "prep", "route")
 
 
 def dsa_profile_start(max_launches: int = 65536):

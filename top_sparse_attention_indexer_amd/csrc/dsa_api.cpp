@@ -258,6 +258,19 @@ dsa_status hip_status(hipError_t e, const char* where) {
   return ok();
 }
 
+dsa_status check_router(const dsa_router* r, dsa::RouterArgs& R) {
+  if (!r) return fail(DSA_ERR_INVALID_ARG, "router is null");
+  if (r->hidden < 1 || r->hidden > 65536)
+    return fail(DSA_ERR_INVALID_ARG, "router hidden %d not in [1, 65536]", r->hidden);
+  DSA_NEED(r->w1, "router w1");
+  DSA_NEED(r->b1, "router b1");
+  DSA_NEED(r->w2, "router w2");
+  DSA_NEED(r->b2, "router b2");
+  R.hidden = r->hidden;
+  R.w1 = r->w1; R.b1 = r->b1; R.w2 = r->w2; R.b2 = r->b2;
+  return DSA_OK;
+}
+
 dsa_status check_gate(const float* gate, const float* y2) {
   if (gate) {
     if (!aligned16(gate)) return fail(DSA_ERR_INVALID_ARG, "gate is not 16-byte aligned");
@@ -493,6 +506,71 @@ dsa_status dsa_fused_forward(const dsa_problem* p, const void* q_idx, const void
     }
   }
   return hip_status(e, "dsa_fused_forward");
+}
+
+dsa_status dsa_route_workspace_size(const dsa_problem* p, const dsa_router* r, size_t* bytes) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  dsa::RouterArgs R;
+  if ((st = check_router(r, R)) != DSA_OK) return st;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is null");
+  size_t fwd = 0;   // what every other entry point accepts, the forward included
+  if ((st = dsa_workspace_size(p, &fwd)) != DSA_OK) return st;
+  *bytes = is_empty(D) ? 0 : std::max(dsa::route_ws_bytes(D, R.hidden), fwd);
+  return ok();
+}
+
+dsa_status dsa_route_heads(const dsa_problem* p, const dsa_router* r, const void* k,
+                           uint8_t* route, float* logits, void* ws, size_t ws_bytes,
+                           void* stream) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  dsa::RouterArgs R;
+  if ((st = check_router(r, R)) != DSA_OK) return st;
+  if (is_empty(D)) return ok();
+  DSA_NEED(k, "k");
+  if (!route) return fail(DSA_ERR_INVALID_ARG, "route is null");
+  if (logits && !aligned16(logits)) return fail(DSA_ERR_INVALID_ARG, "logits is not 16-byte aligned");
+  Plan P;
+  P.total = dsa::route_ws_bytes(D, R.hidden);
+  if ((st = check_ws(P, ws, ws_bytes)) != DSA_OK) return st;
+  return hip_status(dsa::launch_route(D, R, k, route, logits, ws, (hipStream_t)stream),
+                    "dsa_route_heads");
+}
+
+dsa_status dsa_fused_forward_routed(const dsa_problem* p, const dsa_router* r, const void* q_idx,
+                                    const void* k_idx, const void* q, const void* k,
+                                    const void* v, const float* gate, const float* y2,
+                                    uint8_t* route_out, float* out, int32_t* topk_idx_out,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  dsa::Dims D;
+  dsa_status st = check_problem(p, D);
+  if (st != DSA_OK) return st;
+  dsa::RouterArgs R;
+  if ((st = check_router(r, R)) != DSA_OK) return st;
+  if (is_empty(D)) return ok();
+  DSA_NEED(route_out, "route_out");
+  DSA_NEED(k, "k");
+  // every check of the forward runs before the router is enqueued
+  size_t need = 0;
+  if ((st = dsa::fused_ws_need(p, &need)) != DSA_OK) return st;
+  Plan P;
+  P.total = std::max(dsa::route_ws_bytes(D, R.hidden), need);
+  if ((st = check_ws(P, ws, ws_bytes)) != DSA_OK) return st;
+  DSA_NEED(q_idx, "q_idx");
+  DSA_NEED(k_idx, "k_idx");
+  DSA_NEED(q, "q");
+  DSA_NEED(v, "v");
+  DSA_NEED(out, "out");
+  if (topk_idx_out && !aligned16(topk_idx_out))
+    return fail(DSA_ERR_INVALID_ARG, "topk_idx_out is not 16-byte aligned");
+  if ((st = check_gate(gate, y2)) != DSA_OK) return st;
+  hipError_t e = dsa::launch_route(D, R, k, route_out, nullptr, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "dsa_fused_forward_routed");
+  return dsa_fused_forward(p, q_idx, k_idx, q, k, v, gate, y2, route_out, out, topk_idx_out, ws,
+                           ws_bytes, stream);
 }
 
 dsa_status dsa_exec_status(const void* ws, void* stream) {

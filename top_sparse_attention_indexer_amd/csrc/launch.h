@@ -138,9 +138,22 @@ void forget_launch(const void* ws);
 // otherwise create (the cross-stream ordering event).
 hipError_t decode_setup();
 
+// ---- route producer (route.hip) -----------------------------------------------
+// Weights of the two-layer router (device pointers, fp32): W1 [Hkv*d, hidden],
+// b1 [hidden], W2 [hidden, Hq, 2], b2 [Hq, 2] (column 0 full, 1 sparse).
+struct RouterArgs {
+  int hidden;
+  const float *w1, *b1, *w2, *b2;
+};
+size_t route_ws_bytes(const Dims& D, int hidden);
+// route [B, Hq] (1 = sparse) and, if logits != nullptr, logits [B, Hq, 2]
+// from the keys k [B, L, Hkv, d] of the last N positions of each sequence.
+hipError_t launch_route(const Dims& D, const RouterArgs& r, const void* k, uint8_t* route,
+                        float* logits, void* ws, hipStream_t s);
+
 // ---- stage timing (dsa_profile_start / dsa_profile_stop) -----------------------
 enum Stage { kStageIndexer = 0, kStageTopk = 1, kStageAttention = 2, kStageMerge = 3,
-             kStageDecode = 4, kStagePrep = 5, kStages = 6 };
+             kStageDecode = 4, kStagePrep = 5, kStageRoute = 6, kStages = 7 };
 void prof_begin(hipStream_t s, int stage);
 void prof_end(hipStream_t s);
 hipError_t prof_start(int max_launches);
