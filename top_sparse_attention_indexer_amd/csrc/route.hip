@@ -15,10 +15,10 @@
 // bytes per sequence); the MLP is a few MB of fp32 weights read per
 // sequence.  Four launches, all in a fixed summation order, so the same
 // input always gives the same decision:
-//   k_route_pool    chunk partial sums of the key rows   grid (chunks, B)
+//   k_route_pool    chunk partial sums of the key rows   grid (C / 128, chunks, B)
 //   k_route_reduce  mean over the chunks                 grid (C / 64, B)
-//   k_route_hidden  first layer + ReLU                   grid (Hr / 64, B)
-//   k_route_out     second layer, logits and decision    grid (2 Hq / 64, B)
+//   k_route_hidden  first layer + ReLU                   grid (Hr / 64, B), 16 waves
+//   k_route_out     second layer, logits and decision    grid (2 Hq / 64, B), 16 waves
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -30,22 +30,27 @@ namespace dsa {
 namespace {
 
 constexpr int RT = 256;
-constexpr int kMinRows = 32;         // key rows per pooling workgroup at least
-constexpr int kPoolGroups = 1024;    // pooling workgroups aimed for (all sequences)
+constexpr int MT = 1024;             // threads of the two layer kernels
+constexpr int kMinRows = 64;         // key rows per pooling workgroup at least
+constexpr int kPoolGroups = 2048;    // pooling workgroups aimed for (all sequences)
+
+// Pooling workgroup: 16 column groups of 8 values x 16 row lanes.
+constexpr int kPoolCols = 16, kPoolLanes = RT / kPoolCols;
 
 struct RoutePlan {
-  int nch, rows;    // chunks per sequence, rows per chunk
+  int ncol, nch, rows;    // column blocks, chunks per sequence, rows per chunk
   size_t part_off, x_off, h_off, total;
 };
 
 RoutePlan route_plan(const Dims& D, int hidden) {
   RoutePlan P;
   const long long n = std::max(1, D.N);
-  long long nch = std::max<long long>(1, kPoolGroups / std::max(1, D.B));
+  const int C = D.Hkv * D.d;
+  P.ncol = (C / 8 + kPoolCols - 1) / kPoolCols;
+  long long nch = std::max<long long>(1, kPoolGroups / ((long long)P.ncol * std::max(1, D.B)));
   nch = std::min(nch, (n + kMinRows - 1) / kMinRows);
   P.rows = (int)((n + nch - 1) / nch);
   P.nch = (int)((n + P.rows - 1) / P.rows);
-  const size_t C = (size_t)D.Hkv * D.d;
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   P.part_off = 0;
   P.x_off = al((size_t)D.B * P.nch * C * 4);
@@ -71,143 +76,142 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Partial sums of the key rows of one chunk: part[b][ch][c].  Thread t takes
-// 8 columns (group t % G8) of every rpar-th row; the rpar partial sums of a
-// group are then added in a fixed order.
+// Partial sums of the key rows of one chunk and one block of 128 columns:
+// part[b][ch][c].  Thread (row lane ro, group g) adds 8 columns of rows
+// ro, ro + 16, ... of the chunk (four loads in flight, added in row order);
+// the 16 row lanes of a group are then added in lane order.
 template <typename T>
 __global__ __launch_bounds__(RT) void k_route_pool(const T* __restrict__ k, int L, int N, int C,
                                                    int rows, int nch, float* __restrict__ part) {
-  __shared__ float red[RT * 8];
-  const int ch = blockIdx.x, b = blockIdx.y;
+  __shared__ float red[kPoolLanes][kPoolCols * 8 + 4];
+  const int cb = blockIdx.x, ch = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x;
+  const int gl = t % kPoolCols, ro = t / kPoolCols;
+  const int g = cb * kPoolCols + gl;
+  const bool gv = g < C / 8;
   const long long j0 = (long long)L - N + (long long)ch * rows;
   const long long j1 = std::min<long long>(L, j0 + rows);
-  const int G8 = C / 8;
-  const T* kb = k + (size_t)b * L * C;
-  float* out = part + ((size_t)b * nch + ch) * C;
-  if (G8 <= RT) {
-    const int rpar = RT / G8;
-    const int g = t % G8, ro = t / G8;
-    float acc[8];
+  const T* kb = k + (size_t)b * L * C + (gv ? g * 8 : 0);
+  float acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    if (ro < rpar) {
-      long long j = j0 + ro;
-      // four rows in flight, added in row order
-      for (; j + 3LL * rpar < j1; j += 4LL * rpar) {
-        float v[4][8];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  if (gv) {
+    long long j = j0 + ro;
+    for (; j + 3LL * kPoolLanes < j1; j += 4LL * kPoolLanes) {
+      float v[4][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) load8(kb + (size_t)(j + (long long)u * rpar) * C + g * 8, v[u]);
+      for (int u = 0; u < 4; ++u) load8(kb + (size_t)(j + (long long)u * kPoolLanes) * C, v[u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
-      }
-      for (; j < j1; j += rpar) {
-        float v[8];
-        load8(kb + (size_t)j * C + g * 8, v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += v[e];
-      }
+        for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[t * 8 + e] = acc[e];
-    __syncthreads();
-    if (t < G8) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float s = red[t * 8 + e];
-        for (int r = 1; r < rpar; ++r) s += red[(r * G8 + t) * 8 + e];
-        out[t * 8 + e] = s;
-      }
-    }
-    return;
-  }
-  // wide rows: each thread walks whole column groups
-  for (int g = t; g < G8; g += RT) {
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (long long j = j0; j < j1; ++j) {
+    for (; j < j1; j += kPoolLanes) {
       float v[8];
-      load8(kb + (size_t)j * C + g * 8, v);
+      load8(kb + (size_t)j * C, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
+  }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[g * 8 + e] = acc[e];
+  for (int e = 0; e < 8; ++e) red[ro][gl * 8 + e] = acc[e];
+  __syncthreads();
+  // one thread per column of the block adds the 16 row lanes
+  if (t < kPoolCols * 8) {
+    const int c = cb * kPoolCols * 8 + t;
+    float s = red[0][t];
+    for (int r = 1; r < kPoolLanes; ++r) s += red[r][t];
+    if (c < C) part[((size_t)b * nch + ch) * C + c] = s;
   }
 }
 
 // x[b][c] = (sum over chunks of part[b][ch][c]) / N; wave w adds chunks
-// w, w + 4, ...; the four wave sums are added in wave order.
+// w, w + 4, ... (eight loads in flight, added in chunk order); the four wave
+// sums are added in wave order.
 __global__ __launch_bounds__(RT) void k_route_reduce(const float* __restrict__ part, int nch, int C,
                                                      int N, float* __restrict__ x) {
   __shared__ float s[4][64];
   const int b = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 64 + lane;
   float acc = 0.f;
-  if (c < C)
-    for (int ch = w; ch < nch; ch += 4) acc += part[((size_t)b * nch + ch) * C + c];
+  if (c < C) {
+    const float* pb = part + (size_t)b * nch * C + c;
+    int ch = w;
+    for (; ch + 28 < nch; ch += 32) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pb[(size_t)(ch + 4 * u) * C];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; ch < nch; ch += 4) acc += pb[(size_t)ch * C];
+  }
   s[w][lane] = acc;
   __syncthreads();
   if (w == 0 && c < C) x[(size_t)b * C + c] = (((s[0][lane] + s[1][lane]) + s[2][lane]) + s[3][lane]) / (float)N;
 }
 
-// hidden[b][u] = max(0, sum_c x[b][c] W1[c][u] + b1[u]); wave w takes the
-// quarter w of the inputs, the quarters are added in wave order.
-__global__ __launch_bounds__(RT) void k_route_hidden(const float* __restrict__ x,
+// Dot products of one vector with 64 columns of a row-major [R, ncols]
+// matrix, R split over the 16 waves (eight rows in flight per lane); the
+// wave sums are added in wave order into red[0][lane].
+__device__ __forceinline__ void gemv64(const float* __restrict__ vec, const float* __restrict__ m,
+                                       int R, int ncols, int col, float (*red)[64]) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = (R + 15) / 16;
+  const int r0 = w * q, r1 = std::min(R, r0 + q);
+  float acc = 0.f;
+  if (col < ncols) {
+    int r = r0;
+    for (; r + 7 < r1; r += 8) {
+      float a[8], v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a[u] = vec[r + u];
+        v[u] = m[(size_t)(r + u) * ncols + col];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(a[u], v[u], acc);
+    }
+    for (; r < r1; ++r) acc = fmaf(vec[r], m[(size_t)r * ncols + col], acc);
+  }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    float t = red[0][lane];
+    for (int i = 1; i < 16; ++i) t += red[i][lane];
+    red[0][lane] = t;
+  }
+}
+
+// hidden[b][u] = max(0, sum_c x[b][c] W1[c][u] + b1[u]) for 64 units u.
+__global__ __launch_bounds__(MT) void k_route_hidden(const float* __restrict__ x,
                                                      const float* __restrict__ w1,
                                                      const float* __restrict__ b1, int C, int Hr,
                                                      float* __restrict__ hid) {
-  __shared__ float s[4][64];
-  const int b = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float red[16][64];
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
   const int u = blockIdx.x * 64 + lane;
-  const int q = (C + 3) / 4;
-  const int c0 = w * q, c1 = std::min(C, c0 + q);
-  const float* xb = x + (size_t)b * C;
-  float acc = 0.f;
-  if (u < Hr) {
-    int c = c0;
-    for (; c + 3 < c1; c += 4) {
-      const float w0 = w1[(size_t)c * Hr + u], w1v = w1[(size_t)(c + 1) * Hr + u];
-      const float w2v = w1[(size_t)(c + 2) * Hr + u], w3v = w1[(size_t)(c + 3) * Hr + u];
-      acc = fmaf(xb[c], w0, acc);
-      acc = fmaf(xb[c + 1], w1v, acc);
-      acc = fmaf(xb[c + 2], w2v, acc);
-      acc = fmaf(xb[c + 3], w3v, acc);
-    }
-    for (; c < c1; ++c) acc = fmaf(xb[c], w1[(size_t)c * Hr + u], acc);
-  }
-  s[w][lane] = acc;
-  __syncthreads();
-  if (w == 0 && u < Hr) {
-    const float a = (((s[0][lane] + s[1][lane]) + s[2][lane]) + s[3][lane]) + b1[u];
+  gemv64(x + (size_t)b * C, w1, C, Hr, u, red);
+  if (threadIdx.x < 64 && u < Hr) {
+    const float a = red[0][lane] + b1[u];
     hid[(size_t)b * Hr + u] = a > 0.f ? a : 0.f;
   }
 }
 
-// z[b][o] = sum_u hidden[b][u] W2[u][o] + b2[o] for o < 2 Hq; the pair
-// (2h, 2h + 1) of head h sits in neighbouring lanes of wave 0.
-__global__ __launch_bounds__(RT) void k_route_out(const float* __restrict__ hid,
+// z[b][o] = sum_u hidden[b][u] W2[u][o] + b2[o] for 64 outputs o < 2 Hq;
+// the pair (2h, 2h + 1) of head h sits in neighbouring lanes of wave 0.
+__global__ __launch_bounds__(MT) void k_route_out(const float* __restrict__ hid,
                                                   const float* __restrict__ w2,
                                                   const float* __restrict__ b2, int Hr, int Hq,
                                                   float* __restrict__ logits,
                                                   uint8_t* __restrict__ route) {
-  __shared__ float s[4][64];
-  const int b = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float red[16][64];
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
   const int O = 2 * Hq;
   const int o = blockIdx.x * 64 + lane;
-  const int q = (Hr + 3) / 4;
-  const int u0 = w * q, u1 = std::min(Hr, u0 + q);
-  const float* hb = hid + (size_t)b * Hr;
-  float acc = 0.f;
-  if (o < O)
-    for (int u = u0; u < u1; ++u) acc = fmaf(hb[u], w2[(size_t)u * O + o], acc);
-  s[w][lane] = acc;
-  __syncthreads();
-  if (w == 0) {
-    const float z = o < O ? (((s[0][lane] + s[1][lane]) + s[2][lane]) + s[3][lane]) + b2[o] : 0.f;
+  gemv64(hid + (size_t)b * Hr, w2, Hr, O, o, red);
+  if (threadIdx.x < 64) {
+    const float z = o < O ? red[0][lane] + b2[o] : 0.f;
     const float other = __shfl_xor(z, 1);
     if (o < O) {
       if (logits) logits[(size_t)b * O + o] = z;
@@ -230,7 +234,7 @@ hipError_t launch_route(const Dims& D, const RouterArgs& r, const void* k, uint8
   float* x = (float*)(w + P.x_off);
   float* hid = (float*)(w + P.h_off);
   ProfScope ps(s, kStageRoute);
-  const dim3 gp(P.nch, D.B);
+  const dim3 gp(P.ncol, P.nch, D.B);
   if (D.qkv_bf16)
     hipLaunchKernelGGL(k_route_pool<bf16_bits>, gp, dim3(RT), 0, s, (const bf16_bits*)k, D.L, D.N,
                        C, P.rows, P.nch, part);
@@ -239,9 +243,9 @@ hipError_t launch_route(const Dims& D, const RouterArgs& r, const void* k, uint8
                        P.rows, P.nch, part);
   hipLaunchKernelGGL(k_route_reduce, dim3((C + 63) / 64, D.B), dim3(RT), 0, s, part, P.nch, C,
                      D.N, x);
-  hipLaunchKernelGGL(k_route_hidden, dim3((r.hidden + 63) / 64, D.B), dim3(RT), 0, s, x, r.w1,
+  hipLaunchKernelGGL(k_route_hidden, dim3((r.hidden + 63) / 64, D.B), dim3(MT), 0, s, x, r.w1,
                      r.b1, C, r.hidden, hid);
-  hipLaunchKernelGGL(k_route_out, dim3((2 * D.Hq + 63) / 64, D.B), dim3(RT), 0, s, hid, r.w2, r.b2,
+  hipLaunchKernelGGL(k_route_out, dim3((2 * D.Hq + 63) / 64, D.B), dim3(MT), 0, s, hid, r.w2, r.b2,
                      r.hidden, D.Hq, logits, route);
   return hipGetLastError();
 }
