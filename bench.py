@@ -346,6 +346,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="only the headline workload")
+    ap.add_argument("--router-only", action="store_true",
+                    help="time only the route producer on the workload's keys (one JSON line)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the workload, copy this many bytes device to device "
                          "(a plain copy kernel of known size, for counter calibration)")
@@ -367,6 +369,15 @@ def main():
     from top_sparse_attention_indexer_amd import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.router_only:
+        progress(f"{w.name}: inputs")
+        rr = RoutedRunner(Runner(w), router_only=True)
+        ms_r, spread_r, stages_r = timed([rr], args.steps, args.warmup)
+        mr = dict(work_model(w, rr.route.cpu().numpy()), route_bytes=rr.route_bytes())
+        print(json.dumps({"workload": w.name, "router_ms": ms_r, "step_ms_p10_p50_p90": spread_r,
+                          "stages": stage_rooflines(w, mr, stages_r, args.steps),
+                          "hidden": rr.hidden, "route_bytes": rr.route_bytes()}))
+        return
     head, runners, m = measure(w, args.steps, args.warmup)
     st = head["stages"]
     # dominant kernel: the stage with the largest GPU time
