@@ -13,7 +13,7 @@
 //     score range and a 256-bin histogram; the threshold tau is the lower
 //     edge of the bin that brings the count from the top to about
 //     1.5 K * samples / visible (no threshold when that covers every key).
-//   k_idx_scan<false>: workgroups of 64 rows x 512 keys count, per (row, key
+//   k_idx_scan<false>: workgroups of 64 rows x 256 keys count, per (row, key
 //     chunk), the scores >= tau; k_idx_offsets turns the counts into each
 //     chunk's offset in the row's candidate list;
 //   k_idx_scan<true>: the same tiles again, appending (score, position) of
