@@ -241,7 +241,9 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
   const int kb = c * a.RC;
   const int ke = min(kb + a.RC, pmax + 1);       // keys [kb, ke) of the range
   const int wlast = min(a.R - 1, rbase + w * 32 + 31);
-  const int pmax_wave = off + wlast;
+  // wave-uniform (read from lane 0 so that the branches on it stay scalar)
+  const int pmax_wave = __builtin_amdgcn_readfirstlane(off + wlast);
+  const int pmin_wave = __builtin_amdgcn_readfirstlane(off + rbase + w * 32);
   bf16x8 qb[2][T];
   int prow[2];
   bool rvalid[2];
@@ -315,19 +317,29 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
         }
       }
       // raw scores; masks only where a key can lie past a row's position or
-      // the range (the wave's first row has the smallest position)
-      const bool interior = j0 + DKEYS - 1 <= off + rbase + w * 32 && j0 + DKEYS <= ke;
+      // the range (the wave's first row has the smallest position).  The
+      // test is wave-uniform and the masked form uses plain selects, so the
+      // step has no per-element branches.
+      const bool interior = j0 + DKEYS - 1 <= pmin_wave && j0 + DKEYS <= ke;
       bf16x8 pb[2][2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         float sv[16];
+        if (interior) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int j = j0 + u * 16 + 4 * q + rr;
-            sv[u * 4 + rr] = (interior || (j <= prow[cc] && j < ke)) ? sacc[cc][u][rr] : -INFINITY;
-          }
+            for (int rr = 0; rr < 4; ++rr) sv[u * 4 + rr] = sacc[cc][u][rr];
+        } else {
+          const int lim = min(prow[cc] + 1, ke);   // keys below lim are visible
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int j = j0 + u * 16 + 4 * q + rr;
+              sv[u * 4 + rr] = j < lim ? sacc[cc][u][rr] : -INFINITY;
+            }
+        }
         float mt = sv[0];
 #pragma unroll
         for (int x = 1; x < 16; ++x) mt = fmaxf(mt, sv[x]);
@@ -344,14 +356,12 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
           st[cc].l *= alpha;
           st[cc].m = mnew;
         }
+        // a column whose maximum is still -inf has only masked scores, which
+        // give exp2(-inf) = 0 against any finite subtrahend
+        const float msub = st[cc].m == -INFINITY ? 0.f : st[cc].m;
         float pv[16];
-        if (st[cc].m == -INFINITY) {
 #pragma unroll
-          for (int x = 0; x < 16; ++x) pv[x] = 0.f;
-        } else {
-#pragma unroll
-          for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(fmaf(sv[x], a.scale_log2, -st[cc].m));
-        }
+        for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(fmaf(sv[x], a.scale_log2, -msub));
         float ps = 0.f;
 #pragma unroll
         for (int x = 0; x < 16; ++x) ps += pv[x];

@@ -156,14 +156,12 @@ __device__ __forceinline__ void step32_lds(const char* ktile, const char* vtile,
     st.l *= alpha;
     st.m = mnew;
   }
+  // a column whose maximum is still -inf has only masked scores, which give
+  // exp2(-inf) = 0 against any finite subtrahend
+  const float msub = st.m == -INFINITY ? 0.f : st.m;
   float p[8];
-  if (st.m == -INFINITY) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) p[x] = 0.f;
-  } else {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) p[x] = exp2_fast(fmaf(s[x], c, -st.m));
-  }
+  for (int x = 0; x < 8; ++x) p[x] = exp2_fast(fmaf(s[x], c, -msub));
   float ps = 0.f;
 #pragma unroll
   for (int x = 0; x < 8; ++x) ps += p[x];
