@@ -271,22 +271,38 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
   }
   const bf16_bits* kbase = a.k + ((size_t)b * a.L * a.Hkv + g) * HD;
   const bf16_bits* vbase = a.v + ((size_t)b * a.L * a.Hkv + g) * HD;
+  // each step reads through buffer resources based at its first row, so
+  // each lane's row and chunk is a fixed vector offset and the range check
+  // (which covers the vector offset) turns rows past the sequence into
+  // zeros; rows past the range are real keys of the sequence (their scores
+  // are masked, their values weighted 0)
+  const uint32_t rs_bytes = (uint32_t)(a.Hkv * HD * 2);
   const size_t rstride = (size_t)a.Hkv * HD;
-  // the 64 key and value rows from j0 into buffer buf; rows past the range
-  // read its last row (their scores are masked)
-  auto issue = [&](int j0, int buf) {
+  constexpr int MPW = DKEYS / RPI / 4;           // direct loads per wave and buffer
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t ko[MPW], vo[MPW];
 #pragma unroll
-    for (int m = w; m < DKEYS / RPI; m += 4) {
-      const int rr = m * RPI + lane / CPR, pc = lane % CPR;
-      const size_t j = (size_t)min(j0 + rr, ke - 1);
-      const int lck = pc ^ (rr & (CPR - 1));
-      const int lcv = pc ^ ((rr & (CPR / 2 - 1)) << 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + j * rstride + lck * 8),
-                                       (__attribute__((address_space(3))) void*)(kbuf0 + buf * TB + m * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + j * rstride + lcv * 8),
-                                       (__attribute__((address_space(3))) void*)(vbuf0 + buf * TB + m * 1024),
-                                       16, 0, 0);
+  for (int x = 0; x < MPW; ++x) {
+    const int rr = (wu + 4 * x) * RPI + lane / CPR, pc = lane % CPR;
+    ko[x] = (uint32_t)rr * rs_bytes + (uint32_t)((pc ^ (rr & (CPR - 1))) * 16);
+    vo[x] = (uint32_t)rr * rs_bytes + (uint32_t)((pc ^ ((rr & (CPR / 2 - 1)) << 1)) * 16);
+  }
+  // the 64 key and value rows from j0 into buffer buf
+  auto issue = [&](int j0, int buf) {
+    const int nrec = (int)((uint32_t)(a.L - 1 - j0) * rs_bytes + HD * 2);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (size_t)j0 * rstride), (short)0, nrec, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (size_t)j0 * rstride), (short)0, nrec, kBufWord3);
+#pragma unroll
+    for (int x = 0; x < MPW; ++x) {
+      const int m = wu + 4 * x;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (__attribute__((address_space(3))) void*)(kbuf0 + buf * TB + m * 1024), 16, ko[x], 0,
+          0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(vbuf0 + buf * TB + m * 1024), 16, vo[x], 0,
+          0, 0);
     }
   };
   const int nsteps = (ke - kb + DKEYS - 1) / DKEYS;
