@@ -242,8 +242,38 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
   float2* clist = a.cand + row * a.cap;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();                               // the whole tile has landed
-  // this wave's rows see keys up to p_w
-  const int p_w = a.L - a.N + (a.n0 + min(a.R - 1, r0 + 15)) / a.rpt;
+  // this wave's rows see keys up to p_w; keys up to p_w0 (its first row's
+  // position) are visible to every row of the wave (wave-uniform values)
+  const int p_w = __builtin_amdgcn_readfirstlane(a.L - a.N + (a.n0 + min(a.R - 1, r0 + 15)) / a.rpt);
+  const int p_w0 = __builtin_amdgcn_readfirstlane(a.L - a.N + (a.n0 + r0) / a.rpt);
+  // a row without a list has tau = +inf, so no score passes it
+  const int lim = need ? p + 1 : 0;                // keys below lim are visible
+  if (!WRITE) {
+    // counts only: per lane over the tiles, across the quads once at the end
+    uint32_t cnt = 0;
+    if (r0 < a.R && j_lo <= p_w) {
+      for (int j0 = j_lo; j0 < j_hi && j0 <= p_w; j0 += 16) {
+        const int u = (j0 - j_lo) >> 4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(ktile + kt_swz<DIDX>(u * 16 + i, 4 * t + q));
+          acc = mfma16(as_bf16x8(kv), qb[t], acc);
+        }
+        if (j0 + 15 <= p_w0) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) cnt += acc[x] >= tau ? 1u : 0u;
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) cnt += (j0 + 4 * q + x < lim && acc[x] >= tau) ? 1u : 0u;
+        }
+      }
+    }
+    cnt += __shfl_xor(cnt, 16, 64);
+    cnt += __shfl_xor(cnt, 32, 64);
+    if (need && q == 0) *cc = (int)cnt;
+    return;
+  }
   if (r0 < a.R && j_lo <= p_w) {
     for (int j0 = j_lo; j0 < j_hi && j0 <= p_w; j0 += 16) {
       const int u = (j0 - j_lo) >> 4;
@@ -255,10 +285,7 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
       }
       uint32_t bits = 0;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int j = j0 + 4 * q + x;
-        bits |= (need && j <= p && acc[x] >= tau) ? (1u << x) : 0u;
-      }
+      for (int x = 0; x < 4; ++x) bits |= (j0 + 4 * q + x < lim && acc[x] >= tau) ? (1u << x) : 0u;
       const uint32_t c = __popc(bits);
       // counts of the column's quads (lane 16 q + i): prefix over q
       const uint32_t c1 = __shfl_xor(c, 16, 64);            // quad q ^ 1
@@ -278,7 +305,6 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
       run += (int)(pair + pair2);
     }
   }
-  if (!WRITE && need && q == 0) *cc = run;
 }
 
 // Counts of a row's key chunks -> their offsets in the row's list (in
