@@ -116,26 +116,40 @@ __global__ __launch_bounds__(FT) void k_idx_tau(FilterArgs a) {
   // sample: keys s * stride, s = 0 .. ns - 1, over the wave's range
   const int stride = max(1, (p_hi + kSamples) / kSamples);
   const int ns = p_hi / stride + 1;            // samples of the longest row
-  float mn = INFINITY, mx = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += 16) {
-    // A operand rows: sample keys (s0 + i) * stride
-    uint4 kb[T];
-    const int js = (s0 + i) * stride;
+  // scores of the sample blocks s0 .. s0 + 16 SU - 1 (A operand rows: sample
+  // keys (s0 + 16 uu + i) * stride), SU blocks of loads in flight together
+  constexpr int SU = 8;
+  auto sample_scores = [&](int s0, f32x4 (&acc)[SU]) {
+    uint4 kb[SU][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-      kb[t] = (s0 + i < ns) ? *reinterpret_cast<const uint4*>(kseq + (size_t)js * DIDX + t * 32 + q * 8)
-                            : make_uint4(0, 0, 0, 0);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int uu = 0; uu < SU; ++uu) {
+      const int sx = s0 + uu * 16 + i;
+      const size_t js = (size_t)min(sx, ns - 1) * stride;
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(kb[t]), qb[t], acc);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int sidx = s0 + 4 * q + x;
-      if (sidx < ns && sidx * stride <= p) {
-        mn = fminf(mn, acc[x]);
-        mx = fmaxf(mx, acc[x]);
-      }
+      for (int t = 0; t < T; ++t)
+        kb[uu][t] = *reinterpret_cast<const uint4*>(kseq + js * DIDX + t * 32 + q * 8);
     }
+#pragma unroll
+    for (int uu = 0; uu < SU; ++uu) {
+      acc[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[uu] = mfma16(as_bf16x8(kb[uu][t]), qb[t], acc[uu]);
+    }
+  };
+  float mn = INFINITY, mx = -INFINITY;
+  for (int s0 = 0; s0 < ns; s0 += 16 * SU) {
+    f32x4 acc[SU];
+    sample_scores(s0, acc);
+#pragma unroll
+    for (int uu = 0; uu < SU; ++uu)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int sidx = s0 + uu * 16 + 4 * q + x;
+        if (sidx < ns && sidx * stride <= p) {
+          mn = fminf(mn, acc[uu][x]);
+          mx = fmaxf(mx, acc[uu][x]);
+        }
+      }
   }
   mn = -max_xor32(max_xor16(-mn));
   mx = max_xor32(max_xor16(mx));
@@ -145,24 +159,19 @@ __global__ __launch_bounds__(FT) void k_idx_tau(FilterArgs a) {
   __builtin_amdgcn_wave_barrier();
   const float span = mx - mn;
   const float scale = span > 0.f ? (float)kBins / span : 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 16) {
-    uint4 kb[T];
-    const int js = (s0 + i) * stride;
+  for (int s0 = 0; s0 < ns; s0 += 16 * SU) {
+    f32x4 acc[SU];
+    sample_scores(s0, acc);
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-      kb[t] = (s0 + i < ns) ? *reinterpret_cast<const uint4*>(kseq + (size_t)js * DIDX + t * 32 + q * 8)
-                            : make_uint4(0, 0, 0, 0);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int uu = 0; uu < SU; ++uu)
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(kb[t]), qb[t], acc);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int sidx = s0 + 4 * q + x;
-      if (need && sidx < ns && sidx * stride <= p) {
-        const int bin = min(kBins - 1, max(0, (int)((acc[x] - mn) * scale)));
-        atomicAdd(&hist[w][i][bin >> 1], 1u << (16 * (bin & 1)));
+      for (int x = 0; x < 4; ++x) {
+        const int sidx = s0 + uu * 16 + 4 * q + x;
+        if (need && sidx < ns && sidx * stride <= p) {
+          const int bin = min(kBins - 1, max(0, (int)((acc[uu][x] - mn) * scale)));
+          atomicAdd(&hist[w][i][bin >> 1], 1u << (16 * (bin & 1)));
+        }
       }
-    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
