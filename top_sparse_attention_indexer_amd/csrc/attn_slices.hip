@@ -311,10 +311,14 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
   __syncthreads();
   const int row0 = 4 * q + (i >> 2);   // value row this lane points at (transposing read)
   const int colb = (i & 3) * 8;
-  for (int sidx = 0; sidx < nsteps; ++sidx) {
+  // steps whose keys this wave's rows reach: a prefix of the tile's steps
+  // (the rest only load for the other waves), so the step body below runs
+  // unconditionally and the accumulators stay in place across iterations
+  const int nsteps_w = pmax_wave < kb ? 0 : min(nsteps, (pmax_wave - kb) / DKEYS + 1);
+  for (int sidx = 0; sidx < nsteps_w; ++sidx) {
     const int j0 = kb + sidx * DKEYS;
     if (sidx + 1 < nsteps) issue(j0 + DKEYS, (sidx + 1) & 1);
-    if (j0 <= pmax_wave) {
+    {
       const char* kt = kbuf0 + (sidx & 1) * TB;
       const char* vt = vbuf0 + (sidx & 1) * TB;
       f32x4 sacc[2][4];
@@ -400,6 +404,11 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
       }
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next step have landed
+    __syncthreads();
+  }
+  for (int sidx = nsteps_w; sidx < nsteps; ++sidx) {
+    if (sidx + 1 < nsteps) issue(kb + (sidx + 1) * DKEYS, (sidx + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 #pragma unroll
