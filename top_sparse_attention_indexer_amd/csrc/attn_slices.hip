@@ -16,11 +16,15 @@
 // a region that fits one XCD's 4 MB L2 they come at about 27 TB/s (measured
 // with a plain gather kernel).  So the keys are cut into ranges of RC
 // positions and the work into slices (sequence, KV head, range): the K/V of
-// one slice (RC * d * 4 bytes; 2 MB for RC = 4096, d = 128) is what the
+// one slice (RC * d * 4 bytes; 4 MB for RC = 8192, d = 128) is what the
 // workgroups of an XCD gather from while they work through that slice.
 // Every (query row, head) gets one partial result per range it sees (its
 // online-softmax state: log2-sum-exp and normalised output), merged by
 // k_merge_ranges; rows that see a single range write the output directly.
+// The range length trades L2 locality against the per-(row, range) costs
+// (partials, their merge, each range's pipeline start): on the 64K elastic
+// prefill 8192 keys beat 4096 (attention 84 vs 91 ms, merge 4.1 vs 5.8 ms)
+// and 16384 (87 ms).
 //
 // Scheduling.  k_sched lists the non-empty slices in (sequence, KV head,
 // range) order and deals them to the 8 XCDs round robin; each XCD has a

@@ -91,7 +91,7 @@ hipError_t launch_attention_mfma(const Dims& D, const AttnArgs& a, hipStream_t s
 // slices XCD by XCD, per-range partials merged afterwards.  Needs
 // slice_ws_bytes(D, R) of workspace for a launch over R query rows, and index
 // rows that are ascending in their valid entries (as dsa_topk writes them).
-constexpr int kSliceKeys = 4096;    // keys per range
+constexpr int kSliceKeys = 8192;    // keys per range
 struct SlicePlan {
   int RC = 0;    // keys per range
   int NC = 0;    // ranges of the longest row
