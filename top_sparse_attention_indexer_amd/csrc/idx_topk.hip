@@ -438,8 +438,9 @@ __device__ void select_stream(const SelectArgs& a, int b, int n, int vis, int32_
 template <int DIDX>
 __global__ __launch_bounds__(CT) void k_topk_cands(SelectArgs a) {
   __shared__ uint32_t hist[2048];
+  // keys only: the positions are read again from the list (in L2) by the
+  // final compaction, which halves the LDS and doubles the resident rows
   __shared__ uint32_t ckey[kCandLds];
-  __shared__ int32_t cpos[kCandLds];
   __shared__ float sc[16 * (CT / 64)];
   __shared__ uint32_t scratch[CT / 64 + 1];
   __shared__ uint32_t res[2];
@@ -468,7 +469,6 @@ __global__ __launch_bounds__(CT) void k_topk_cands(SelectArgs a) {
     const float2 e = cl[x];
     const uint32_t u = radix_key(e.x);
     ckey[x] = u;
-    cpos[x] = __float_as_int(e.y);
     atomicAdd(&hist[u >> 21], 1u);
   }
   __syncthreads();
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(CT) void k_topk_cands(SelectArgs a) {
     const uint32_t tie_rank = block_rank<CT>(eq, scratch, tie_tot);
     const bool sel = gt || (eq && base_tie + tie_rank < kk);
     const uint32_t pos = block_rank<CT>(sel, scratch, sel_tot);
-    if (sel && base_sel + pos < (uint32_t)a.K) o[base_sel + pos] = cpos[x];
+    if (sel && base_sel + pos < (uint32_t)a.K) o[base_sel + pos] = __float_as_int(cl[x].y);
     base_tie += tie_tot;
     base_sel += sel_tot;
   }
