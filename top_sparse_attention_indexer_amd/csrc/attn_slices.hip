@@ -649,52 +649,62 @@ __global__ __launch_bounds__(ST) void k_merge_ranges(SliceArgs a) {
   const int n = a.n0 + r, p = a.L - a.N + n;
   const int nr = p / a.RC + 1;
   if (nr == 1) return;
-  constexpr int TPH = HD / 16;            // threads per head
+  constexpr int TPH = HD / 4;             // threads per head: one float4 of the output each
   constexpr int HPR = ST / TPH;           // heads per round
-  const int hl = threadIdx.x / TPH, d0 = (threadIdx.x % TPH) * 16;
+  constexpr int MR = 8;                   // ranges held in registers at once
+  const int hl = threadIdx.x / TPH, d4 = threadIdx.x % TPH;
   for (int h0 = 0; h0 < a.Hq; h0 += HPR) {
     const int h = h0 + hl;
     if (h >= a.Hq) break;
-    float m = -INFINITY;
-    for (int c = 0; c < nr; ++c)
-      m = fmaxf(m, a.part_lse[(((size_t)b * a.R + r) * a.NC + c) * a.Hq + h]);
-    float acc[16];
+    const size_t slot0 = ((size_t)b * a.R + r) * a.NC * a.Hq + h;   // range c at + c * Hq
+    float m = -INFINITY, wsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    // up to MR ranges per round, every load of the round in flight together
+    // (the range count is the same for the whole workgroup)
+    for (int c0 = 0; c0 < nr; c0 += MR) {
+      float lv[MR];
+      float4 ov[MR];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) acc[x] = 0.f;
-    float wsum = 0.f;
-    if (m != -INFINITY) {
-      for (int c = 0; c < nr; ++c) {
-        const size_t slot = (((size_t)b * a.R + r) * a.NC + c) * a.Hq + h;
-        const float lse = a.part_lse[slot];
-        if (lse == -INFINITY) continue;
-        const float wgt = exp2_fast(lse - m);
-        wsum += wgt;
-        const float4* src = reinterpret_cast<const float4*>(a.part_o + slot * HD + d0);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float4 v = src[x];
-          acc[4 * x] = fmaf(wgt, v.x, acc[4 * x]);
-          acc[4 * x + 1] = fmaf(wgt, v.y, acc[4 * x + 1]);
-          acc[4 * x + 2] = fmaf(wgt, v.z, acc[4 * x + 2]);
-          acc[4 * x + 3] = fmaf(wgt, v.w, acc[4 * x + 3]);
+      for (int x = 0; x < MR; ++x) {
+        if (c0 + x < nr) {
+          const size_t slot = slot0 + (size_t)(c0 + x) * a.Hq;
+          lv[x] = a.part_lse[slot];
+          ov[x] = reinterpret_cast<const float4*>(a.part_o + slot * HD)[d4];
+        } else {
+          lv[x] = -INFINITY;
+          ov[x] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
+      float mb = m;
+#pragma unroll
+      for (int x = 0; x < MR; ++x) mb = fmaxf(mb, lv[x]);
+      if (mb == -INFINITY) continue;
+      // a range without entries has lse = -inf (weight 0) and a zero output
+      const float f0 = m == -INFINITY ? 0.f : exp2_fast(m - mb);
+      wsum *= f0;
+      acc.x *= f0; acc.y *= f0; acc.z *= f0; acc.w *= f0;
+#pragma unroll
+      for (int x = 0; x < MR; ++x) {
+        const float wg = lv[x] == -INFINITY ? 0.f : exp2_fast(lv[x] - mb);
+        wsum += wg;
+        acc.x = fmaf(wg, ov[x].x, acc.x);
+        acc.y = fmaf(wg, ov[x].y, acc.y);
+        acc.z = fmaf(wg, ov[x].z, acc.z);
+        acc.w = fmaf(wg, ov[x].w, acc.w);
+      }
+      m = mb;
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     const size_t orow = ((size_t)b * a.N + n) * a.Hq + h;
-    const float gt = a.gate ? a.gate[orow] : 1.f;
-    float4* dst = reinterpret_cast<float4*>(a.out + orow * HD + d0);
+    float o[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    if (a.gate) {
+      const float gt = a.gate[orow];
+      const float4 y = reinterpret_cast<const float4*>(a.y2 + orow * HD)[d4];
+      const float yv[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      float o[4];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        float val = acc[4 * x + y] * inv;
-        if (a.gate) val = fmaf(gt, val, (1.f - gt) * a.y2[orow * HD + d0 + 4 * x + y]);
-        o[y] = val;
-      }
-      dst[x] = make_float4(o[0], o[1], o[2], o[3]);
+      for (int x = 0; x < 4; ++x) o[x] = fmaf(gt, o[x], (1.f - gt) * yv[x]);
     }
+    reinterpret_cast<float4*>(a.out + orow * HD)[d4] = make_float4(o[0], o[1], o[2], o[3]);
   }
 }
 
