@@ -125,7 +125,10 @@ dsa_status dsa_topk(const dsa_problem* p, const float* scores, int32_t* topk_idx
  *   sparse head (route[b,h] = 1, or route == NULL):
  *     a = softmax_j(q . k_j * scale) v_j over j in topk_idx[b,n,h/(Hq/H),:];
  *     entries outside [0, p] (padding) are skipped; a row with no valid entry
- *     gives a = 0;
+ *     gives a = 0.  Precondition: each index row lists its entries in
+ *     [0, p] in ascending order, before any padding (the layout dsa_topk
+ *     writes); prefill shapes read each key range's entries as one
+ *     contiguous run of the row, so other orders can drop entries;
  *   dense head (route[b,h] = 0): the same over every j in 0..p, topk ignored;
  *   out = g*a + (1-g)*y2 with g = gate[b,n,h]; gate == NULL gives out = a
  *   (y2 may then be NULL).
