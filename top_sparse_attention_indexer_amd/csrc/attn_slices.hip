@@ -148,37 +148,38 @@ __global__ __launch_bounds__(ST) void k_sched(SliceArgs a, int32_t* sched) {
 
 // One wave per index row (token row and indexer head): offsets of the ranges
 // in the row.  off[c] = number of valid entries (in [0, p]) below c * RC,
-// for c = 0 .. nr (nr = p / RC + 1); for ascending rows the entries of range
-// c are [off[c], off[c + 1]).
+// for c = 0 .. nr (nr = p / RC + 1).  The row lists its valid entries in
+// ascending order before any padding, so the entries of range c are
+// [off[c], off[c + 1]) and off[c] is where the row's range index first
+// reaches c: found by comparing each entry's range with its predecessor's
+// (no atomics).
 __global__ __launch_bounds__(ST) void k_range_offsets(SliceArgs a) {
-  __shared__ int hist[4][257];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long row = (long long)blockIdx.x * 4 + w;   // ((b * R + r) * IH + ih)
-  if (row >= (long long)a.B * a.R * a.IH) return;   // wave-uniform; no block barrier below
+  if (row >= (long long)a.B * a.R * a.IH) return;   // wave-uniform
   const int ih = (int)(row % a.IH);
   const long long br = row / a.IH;
   const int b = (int)(br / a.R), r = (int)(br - (long long)b * a.R);
   const int n = a.n0 + r, p = a.L - a.N + n;
   const int nr = p / a.RC + 1;
-  int* h = hist[w];
-  for (int c = lane; c <= nr; c += 64) h[c] = 0;
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
   const int32_t* irow =
       a.topk + (((size_t)b * a.idx_rows_per_b + (n - a.idx_n_base)) * a.IH + ih) * a.K;
-  for (int e = lane; e < a.K; e += 64) {
-    const int j = irow[e];
-    if (j >= 0 && j <= p) atomicAdd(&h[j / a.RC + 1], 1);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  if (lane == 0) {
-    int32_t* o = const_cast<int32_t*>(a.off) + (size_t)row * (a.NC + 1);
-    int run = 0;
-    for (int c = 0; c <= nr; ++c) {
-      run += h[c];
-      o[c] = run;
-    }
+  int32_t* o = const_cast<int32_t*>(a.off) + (size_t)row * (a.NC + 1);
+  // range index of an entry; padding, entries past p and the slot past the
+  // row's end count as range nr
+  auto range_of = [&](int j) { return (j >= 0 && j <= p) ? j / a.RC : nr; };
+  // 64 consecutive entries per round (lane = entry, coalesced); a lane whose
+  // entry starts a new range writes that range's offset (and those of any
+  // empty ranges before it); the slot at index K closes the remaining ranges
+  int carry = -1;                                // range of the entry before the round
+  for (int e0 = 0; e0 <= a.K; e0 += 64) {
+    const int e = e0 + lane;
+    const int cur = (e < a.K) ? range_of(irow[e]) : nr;
+    int prev = __shfl_up(cur, 1, 64);
+    if (lane == 0) prev = carry;
+    if (e <= a.K)
+      for (int cc = prev + 1; cc <= cur; ++cc) o[cc] = e;
+    carry = __builtin_amdgcn_readlane(cur, 63);
   }
 }
 
