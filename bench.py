@@ -308,6 +308,45 @@ def timed(runners, steps, warmup):
     return ms, [float(np.percentile(per, q)) for q in (10, 50, 90)], stages
 
 
+def graph_decode(w, steps, warmup):
+    """The decode step captured once into a HIP graph (on a side stream) and
+    replayed `steps` times back to back between two events; the replayed
+    output is compared with the eager one."""
+    import torch
+    r = Runner(w)
+    s = torch.cuda.Stream()
+    r.stream = s
+    with torch.cuda.stream(s):
+        for _ in range(max(2, warmup)):
+            r.step()
+    torch.cuda.synchronize()
+    ref = r.out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        r.step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            g.replay()
+        t0.record(s)
+        for _ in range(steps):
+            g.replay()
+        t1.record(s)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    r.B.dsa_exec_status(r.ws, s)
+    same = bool(torch.equal(r.out, ref))
+    m = work_model(w, r.x["route"])
+    return {"value": w.batch * w.n_q / (ms / 1e3), "unit": "query tokens/s", "ms_per_step": ms,
+            "replays": steps, "replay_matches_eager": same, "config": config_of(w),
+            "stages": {"decode": {"ms": ms, "launches": 1.0, "bound": "hbm",
+                                  "achieved": m["bytes"] / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s",
+                                  "frac": m["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}}
+
+
 def config_of(w):
     return {"workload": w.name, "batch": w.batch, "n_q": w.n_q, "kv_len": w.kv_len,
             "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim, "idx_dim": w.idx_dim,
@@ -432,6 +471,12 @@ def main():
             others[name] = r
             del rr
             torch.cuda.empty_cache()
+        # the batch-8 decode captured into a HIP graph and replayed
+        progress("decode_b8_ctx128k: graph capture and replay")
+        r = graph_decode(synth.WORKLOADS["decode_b8_ctx128k"], 50, 5)
+        progress(f"decode_b8_ctx128k (graph): {r['ms_per_step']:.4f} ms per step")
+        others["decode_b8_ctx128k_graph"] = r
+        torch.cuda.empty_cache()
         # the batch-8 decode with two input sets in alternation (403 MB of
         # inputs, above the 256 MB Infinity Cache)
         wo = synth.WORKLOADS["decode_b8_ctx128k"]

@@ -88,6 +88,7 @@ struct DecodeArgs {
   int ccnt;          // candidates present per row
   float scale_log2;
   uint32_t epoch;    // distinct per launch; tags every control word
+  const uint32_t* epw;  // under stream capture: device word with the launch's epoch
   uint32_t spin_limit;  // polls before a wait gives up (0: give up at the first wait)
 };
 
@@ -124,7 +125,8 @@ constexpr int kBarGroup = 16;   // workgroups per first-level barrier group
 constexpr int kCandGroups = 16;
 // Control block of 64-bit words, each (launch epoch << 32 | value); a word
 // whose epoch is not the current launch's means "nothing yet", so the block
-// is never cleared.  Layout: [0] error word; member slots from word 8 (one
+// is never cleared.  Layout: [0] error word; [1] (seed, count) and [2] epoch
+// of captured launches (k_decode_epoch); member slots from word 8 (one
 // per workgroup).  The sequence barriers' group slots and the verdict words
 // are tagged the same way.
 size_t ctl_words64(int grid) { return 8 + (size_t)grid; }
@@ -133,8 +135,8 @@ __device__ __forceinline__ bool tagged(uint64_t v, uint32_t epoch, uint32_t at_l
   return (uint32_t)(v >> 32) == epoch && (uint32_t)v >= at_least;
 }
 
-__device__ __forceinline__ void raise_error(const DecodeArgs& a, int b) {
-  const uint64_t tag = ((uint64_t)a.epoch << 32) | 1ull;
+__device__ __forceinline__ void raise_error(const DecodeArgs& a, uint32_t ep, int b) {
+  const uint64_t tag = ((uint64_t)ep << 32) | 1ull;
   st_dev64(a.seqerr + 8 * b, tag);
   st_dev64(a.ctl, tag);
 }
@@ -144,18 +146,18 @@ __device__ __forceinline__ void raise_error(const DecodeArgs& a, int b) {
 // when another unit of the sequence already gave up.  A give-up is recorded
 // in the sequence's abort word and in the launch's error word (control word
 // 0), which the host reads back through dsa_exec_status.
-__device__ __forceinline__ bool wait_tag(const DecodeArgs& a, int b, const uint64_t* p,
+__device__ __forceinline__ bool wait_tag(const DecodeArgs& a, uint32_t ep, int b, const uint64_t* p,
                                          uint32_t at_least) {
   if (a.spin_limit == 0) {
-    raise_error(a, b);
+    raise_error(a, ep, b);
     return false;
   }
   uint32_t spins = 0;
-  while (!tagged(ld_dev64(p), a.epoch, at_least)) {
-    if (tagged(ld_dev64(a.seqerr + 8 * b), a.epoch, 1u)) return false;
+  while (!tagged(ld_dev64(p), ep, at_least)) {
+    if (tagged(ld_dev64(a.seqerr + 8 * b), ep, 1u)) return false;
     __builtin_amdgcn_s_sleep(1);
     if (++spins > a.spin_limit) {
-      raise_error(a, b);
+      raise_error(a, ep, b);
       return false;
     }
   }
@@ -170,7 +172,8 @@ __device__ __forceinline__ bool wait_tag(const DecodeArgs& a, int b, const uint6
 // every unit waits for the sequence's group slots.  Each thread first waits
 // for its own outstanding memory operations, so the stores before the
 // barrier have completed when the slot is written.
-__device__ __forceinline__ bool seq_sync(const DecodeArgs& a, int b, uint32_t phase, int* flag) {
+__device__ __forceinline__ bool seq_sync(const DecodeArgs& a, uint32_t ep, int b, uint32_t phase,
+                                         int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int u0 = b * a.nch;
@@ -179,7 +182,7 @@ __device__ __forceinline__ bool seq_sync(const DecodeArgs& a, int b, uint32_t ph
   const int gi = lu / kBarGroup;
   uint64_t* mslot = a.ctl + 8;
   uint64_t* gslot = a.sgslot + (size_t)b * ngs * 8;
-  const uint64_t tag = ((uint64_t)a.epoch << 32) | phase;
+  const uint64_t tag = ((uint64_t)ep << 32) | phase;
   if (threadIdx.x == 0) {
     *flag = 1;
     st_dev64(mslot + blockIdx.x, tag);
@@ -187,13 +190,14 @@ __device__ __forceinline__ bool seq_sync(const DecodeArgs& a, int b, uint32_t ph
   __syncthreads();
   if (lu == gi * kBarGroup) {
     const int gsize = min(kBarGroup, a.nch - gi * kBarGroup);
-    if ((int)threadIdx.x < gsize && !wait_tag(a, b, mslot + u0 + gi * kBarGroup + threadIdx.x, phase))
+    if ((int)threadIdx.x < gsize &&
+        !wait_tag(a, ep, b, mslot + u0 + gi * kBarGroup + threadIdx.x, phase))
       *flag = 0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0 && *flag) st_dev64(gslot + 8 * gi, tag);
   }
-  if ((int)threadIdx.x < ngs && !wait_tag(a, b, gslot + 8 * threadIdx.x, phase)) *flag = 0;
+  if ((int)threadIdx.x < ngs && !wait_tag(a, ep, b, gslot + 8 * threadIdx.x, phase)) *flag = 0;
   __syncthreads();
   return *flag != 0;
 }
@@ -201,7 +205,7 @@ __device__ __forceinline__ bool seq_sync(const DecodeArgs& a, int b, uint32_t ph
 // Row accumulators (both histograms, candidate count, merge tickets) are
 // cleared at the start of every launch by the first unit of the sequence;
 // the row's tag then reads "ready" for this launch.
-__device__ __forceinline__ void clear_rows(const DecodeArgs& a, int b) {
+__device__ __forceinline__ void clear_rows(const DecodeArgs& a, uint32_t ep, int b) {
   const int nt = a.Hkv * a.nhc;
   for (int n = 0; n < a.N; ++n) {
     const int row = b * a.N + n;
@@ -218,15 +222,15 @@ __device__ __forceinline__ void clear_rows(const DecodeArgs& a, int b) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x < a.N)
-    st_dev64(a.rowtag + b * a.N + threadIdx.x, ((uint64_t)a.epoch << 32) | 2ull);
+    st_dev64(a.rowtag + b * a.N + threadIdx.x, ((uint64_t)ep << 32) | 2ull);
 }
 
 // Waits until the rows of sequence b are cleared for this launch.
-__device__ __forceinline__ bool rows_ready(const DecodeArgs& a, int b, int* flag) {
+__device__ __forceinline__ bool rows_ready(const DecodeArgs& a, uint32_t ep, int b, int* flag) {
   __syncthreads();
   if (threadIdx.x == 0) *flag = 1;
   __syncthreads();
-  if ((int)threadIdx.x < a.N && !wait_tag(a, b, a.rowtag + b * a.N + threadIdx.x, 2u)) *flag = 0;
+  if ((int)threadIdx.x < a.N && !wait_tag(a, ep, b, a.rowtag + b * a.N + threadIdx.x, 2u)) *flag = 0;
   __syncthreads();
   return *flag != 0;
 }
@@ -887,7 +891,11 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
   const bool sp = has_unit && seq_sparse(a.route, b, a.Hq);
   const int N = a.N, K = a.K;
 
-  if (has_unit && c == 0) clear_rows(a, b);
+  // the launch's epoch: a kernel argument, or under stream capture (where
+  // every replay of the graph would see the same argument) a word that the
+  // captured k_decode_epoch advanced just before
+  const uint32_t ep = a.epw ? ld_dev(a.epw) : a.epoch;
+  if (has_unit && c == 0) clear_rows(a, ep, b);
   // single-row sequence on the candidate selection
   const bool cand_sel = a.M > 0 && sp && a.L > K;
 
@@ -941,7 +949,7 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
     if (threadIdx.x == 0) res[2] = 0;
   }
   // the sequence's per-row accumulators are cleared by its first unit
-  if (!rows_ready(a, b, &flag)) {
+  if (!rows_ready(a, ep, b, &flag)) {
     abandon<HD>(a, b);
     return;
   }
@@ -1442,7 +1450,7 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       }
       for (int o = (int)base + (int)threadIdx.x; o < a.M; o += DT) st_dev64(cw + o, 0ull);
     }
-    if (!seq_sync(a, b, ph++, &flag)) {
+    if (!seq_sync(a, ep, b, ph++, &flag)) {
       abandon<HD>(a, b);
       return;
     }
@@ -1541,7 +1549,7 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
                       : 0ull;
       const bool valid = ck != 0 && ck > emax;
       if (c == 0 && threadIdx.x == 0)
-        st_dev64(a.verdict + 8 * b, ((uint64_t)a.epoch << 32) | (valid ? 1u : 2u));
+        st_dev64(a.verdict + 8 * b, ((uint64_t)ep << 32) | (valid ? 1u : 2u));
       if (valid) {
         // thread t takes entries [t * per, (t + 1) * per), per <= 32 and even
         const int per = a.Cpad / DT;
@@ -1576,7 +1584,7 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       // sequence falls back (unit 0 publishes the verdict)
       if (threadIdx.x == 0) {
         res[0] = 0;
-        if (wait_tag(a, b, a.verdict + 8 * b, 1u)) res[0] = (uint32_t)ld_dev64(a.verdict + 8 * b);
+        if (wait_tag(a, ep, b, a.verdict + 8 * b, 1u)) res[0] = (uint32_t)ld_dev64(a.verdict + 8 * b);
       }
       __syncthreads();
       const uint32_t vd = res[0];
@@ -1588,14 +1596,14 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
   }
   if (slow) {
     build_hist0();
-    bool ok = seq_sync(a, b, ph++, &flag);
+    bool ok = seq_sync(a, ep, b, ph++, &flag);
     if (ok) {
       cand_phase();
-      ok = seq_sync(a, b, ph++, &flag);
+      ok = seq_sync(a, ep, b, ph++, &flag);
     }
     if (ok) {
       select_phase();
-      ok = seq_sync(a, b, ph++, &flag);
+      ok = seq_sync(a, ep, b, ph++, &flag);
     }
     if (!ok) {
       abandon<HD>(a, b);
@@ -1797,8 +1805,9 @@ std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
 constexpr int kWsSlots = 64;
 struct WsEntry {
   const void* ws;
-  uint32_t epoch;
+  uint32_t epoch;   // the launch's epoch, or kDeviceEpoch: read it from the workspace
 };
+constexpr uint32_t kDeviceEpoch = 0xffffffffu;
 std::mutex g_ws_mu;
 WsEntry g_ws[kWsSlots];
 int g_ws_next = 0;
@@ -1827,10 +1836,12 @@ int decode_exec_status(const void* ws, hipStream_t s, hipError_t* err) {
   }
   *err = hipStreamSynchronize(s);
   if (*err != hipSuccess) return 0;
-  uint64_t word = 0;
-  *err = hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost);
+  // control words 0 (error) .. 2 (the device epoch of captured launches)
+  uint64_t words[3] = {0, 0, 0};
+  *err = hipMemcpy(words, ws, sizeof(words), hipMemcpyDeviceToHost);
   if (*err != hipSuccess) return 0;
-  return word == (((uint64_t)epoch << 32) | 1ull) ? 1 : 0;
+  if (epoch == kDeviceEpoch) epoch = (uint32_t)words[2];
+  return words[0] == (((uint64_t)epoch << 32) | 1ull) ? 1 : 0;
 }
 
 void forget_launch(const void* ws) {
@@ -1847,6 +1858,23 @@ hipError_t decode_setup() {
   std::lock_guard<std::mutex> lock(so.mu);
   if (!so.done) e = hipEventCreateWithFlags(&so.done, hipEventDisableTiming);
   return e;
+}
+
+// Under stream capture the epoch cannot travel as a kernel argument: every
+// replay of the graph would reuse it, and control words left by the previous
+// replay would then pass for this one's.  This one-thread kernel, captured
+// just before the decode kernel, keeps (seed, count) in control words 1-2 and
+// writes the epoch for the launch: a new seed (a new capture) restarts the
+// count, every replay advances it.
+__global__ void k_decode_epoch(uint32_t* w, uint32_t seed) {
+  if (threadIdx.x == 0) {
+    const uint32_t cnt = (w[0] == seed) ? w[1] + 1u : 1u;
+    uint32_t e = seed ^ (cnt * 0x9E3779B9u);
+    if (e == 0) e = 1;
+    w[0] = seed;
+    w[1] = cnt;
+    w[2] = e;   // low half of control word 2
+  }
 }
 
 hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, const void* k_idx,
@@ -1881,20 +1909,39 @@ hipError_t launch_decode(const Dims& D, const DecodePlan& P, const void* q_idx, 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return e;
+  const bool capturing = cs == hipStreamCaptureStatusActive;
   StreamOrder& so = stream_order(dev);
   std::lock_guard<std::mutex> lock(so.mu);
   if (!so.done) {
+    if (capturing) return hipErrorStreamCaptureUnsupported;   // set-up must precede capture
     e = hipEventCreateWithFlags(&so.done, hipEventDisableTiming);
     if (e != hipSuccess) return e;
   }
-  if (so.have_last && so.last != s) {
+  // eager launches on another stream wait for the last one; a captured graph
+  // is ordered against other decode launches by whoever replays it
+  if (!capturing && so.have_last && so.last != s) {
     e = hipStreamWaitEvent(s, so.done, 0);
     if (e != hipSuccess) return e;
   }
   a.epoch = next_epoch(so);
+  a.epw = nullptr;
   a.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
-  record_launch(ws, a.epoch);
   void* args[] = {&a};
+  if (capturing) {
+    uint32_t* w32 = reinterpret_cast<uint32_t*>(a.ctl + 1);   // control words 1-2
+    hipLaunchKernelGGL(k_decode_epoch, dim3(1), dim3(64), 0, s, w32, a.epoch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.epw = w32 + 2;
+    record_launch(ws, kDeviceEpoch);
+    ProfScope ps(s, kStageDecode);
+    e = hipLaunchKernel(select_kernel(D), dim3(P.grid), dim3(DT), args, 0, s);
+    return e;
+  }
+  record_launch(ws, a.epoch);
   // the completion event rides on the kernel's own dispatch
   {
     ProfScope ps(s, kStageDecode);
