@@ -61,6 +61,13 @@
  * some workgroups from starting.  Every wait between workgroups is bounded:
  * a wait that gives up makes the outputs of its sequence NaN and its index
  * rows -1, and dsa_exec_status() then returns DSA_ERR_EXEC.
+ *
+ * Stream capture.  The entry points enqueue only kernels (no copies,
+ * memsets or allocations), so a call can be captured into a HIP graph after
+ * one eager call on the same device (which creates the library's event).
+ * A captured single-launch decode adds a one-thread kernel that advances
+ * the launch tag on the device, so every replay is a fresh launch; replays
+ * of a graph are not ordered by the library against other decode launches.
  */
 #ifndef DSA_H
 #define DSA_H
