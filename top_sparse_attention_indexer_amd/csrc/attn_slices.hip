@@ -453,6 +453,12 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, kBufWord3);
   const int gi = lane / CPR, ch = lane % CPR;
+  // staging lane (gi, ch) fetches chunk ch ^ sp_f(R) of tile row R =
+  // gi * RPG + m and stores it at chunk ch of that row (see sp_f); sp_f is
+  // linear, so the fetched chunk is cfix ^ sp_f(m)
+  const uint32_t cfix = (uint32_t)((ch ^ sp_f<HD>(gi * RPG)) << 4);
+  char* kst = ktile + gi * RPG * (HD * 2) + ch * 16;
+  char* vst = vtile + gi * RPG * (HD * 2) + ch * 16;
   const int kb = c * a.RC;
   const int r1 = min(a.R, r0 + kQB);
   const int HPS = a.Hq / a.IH;              // query heads per index row
@@ -516,7 +522,7 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
         // loaded into registers (whole 256-byte rows per lane group, the
         // access pattern the L2 serves fastest; buffer loads with 32-bit
         // offsets) while step e0 - 32 computes, then written to the wave's
-        // LDS tiles (permuted as kt_swz / vt_swz) and read back as MFMA
+        // LDS tiles (chunks permuted by sp_f) and read back as MFMA
         // operands.  Lane group gi = lane / CPR stages rows gi * RPG ..
         // gi * RPG + RPG - 1.  Entries of -1 read row 0 (masked).
         u32x4 kr[RPG], vr[RPG];
@@ -527,7 +533,7 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
             *reinterpret_cast<int4*>(&jr[m]) = *reinterpret_cast<const int4*>(wl + gi * RPG + m);
 #pragma unroll
           for (int m = 0; m < RPG; ++m) {
-            const uint32_t off = (uint32_t)max(jr[m], 0) * rs_bytes + ch * 16;
+            const uint32_t off = ((uint32_t)max(jr[m], 0) * rs_bytes) | (cfix ^ (uint32_t)(sp_f<HD>(m) << 4));
             kr[m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
             vr[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
           }
@@ -536,9 +542,8 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
           __builtin_amdgcn_s_waitcnt(0);   // this step's rows are in registers
 #pragma unroll
           for (int m = 0; m < RPG; ++m) {
-            const int rr = gi * RPG + m;
-            *reinterpret_cast<u32x4*>(ktile + kt_swz<HD>(rr, ch)) = kr[m];
-            *reinterpret_cast<u32x4*>(vtile + vt_swz<HD>(rr, ch * 16)) = vr[m];
+            *reinterpret_cast<u32x4*>(kst + m * (HD * 2)) = kr[m];
+            *reinterpret_cast<u32x4*>(vst + m * (HD * 2)) = vr[m];
           }
           bool kval[2][4];
 #pragma unroll
@@ -557,7 +562,7 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
                   *reinterpret_cast<const int4*>(wl + e0 + 32 + gi * RPG + m);
 #pragma unroll
             for (int m = 0; m < RPG; ++m) {
-              const uint32_t off = (uint32_t)max(jr[m], 0) * rs_bytes + ch * 16;
+              const uint32_t off = ((uint32_t)max(jr[m], 0) * rs_bytes) | (cfix ^ (uint32_t)(sp_f<HD>(m) << 4));
               kr[m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
               vr[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
             }

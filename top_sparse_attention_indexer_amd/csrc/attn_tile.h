@@ -114,30 +114,69 @@ __device__ __forceinline__ int kt_swz(int R, int c16) {
 // bounded by 2^kLazyLog2 (fine for the fp32 sums and the bf16 P operand).
 constexpr float kLazyLog2 = 8.f;
 
-// 32-key step with both tiles in LDS (rows back to back, permuted as in
-// kt_swz / vt_swz): the key rows are read as the A operand (lane quad q
-// takes bytes 64 t + 16 q of its key row, the order the query operand uses),
-// the value rows with the transposing read.  Raw scores s; the scale c
+// Chunk permutation of the sparse path's key and value tiles: 16-byte chunk
+// c16 of tile row R sits at chunk c16 ^ sp_f(R) of the row (rows back to
+// back, HD * 2 bytes each).  sp_f is a permutation of bits of R, hence
+// linear under xor: sp_f(a ^ b) = sp_f(a) ^ sp_f(b).  It keeps both reads of
+// a tile free of bank conflicts: the key read (sixteen lanes, one chunk of
+// sixteen consecutive rows) meets sixteen different 16-byte bank ranges, and
+// the transposing value read (each 16-lane group, 32 bytes of four
+// consecutive rows) keeps the two chunks of a 32-byte piece together (bit 0
+// of sp_f only swaps them) while the rows' pieces land on different ranges.
+// Because one permutation serves both tiles, the staging lane that loads
+// row R of either tile fetches global chunk ch ^ sp_f(R) and stores it at
+// chunk ch of the tile row: its store addresses differ by whole rows, which
+// the LDS store takes as an immediate offset.
+template <int HD>
+__device__ __forceinline__ int sp_f(int R) {
+  static_assert(HD == 64 || HD == 128, "sparse tiles hold 64- or 128-wide rows");
+  if constexpr (HD == 128) return ((R & 7) << 1) | ((R >> 3) & 1);
+  else return (((R >> 1) & 3) << 1) | ((R >> 3) & 1);
+}
+
+// 32-key step with both tiles in LDS (rows back to back, chunks permuted by
+// sp_f): the key rows are read as the A operand (lane quad q takes logical
+// bytes 64 t + 16 q of its key row, the order the query operand uses), the
+// value rows with the transposing read.  All value reads of the step are
+// issued right after the score MFMAs, so their latency runs under the
+// softmax instead of once per output MFMA.  Raw scores s; the scale c
 // (softmax scale * log2 e) enters through p = exp2(s * c - m).
 template <int HD>
 __device__ __forceinline__ void step32_lds(const char* ktile, const char* vtile,
                                            const bf16x8 (&qb)[HD / 32], const bool (&kvalid)[2][4],
                                            float c, ColState<HD>& st) {
   constexpr int T = HD / 32;
+  constexpr int RB = HD * 2;            // tile row bytes
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, i = lane & 15;
   float s[8];
+  uint4 ka[2][T];
+  const int fi = sp_f<HD>(i);           // rows i and 16 + i permute alike
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    uint4 ka[T];
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int t = 0; t < T; ++t)
-      ka[t] = *reinterpret_cast<const uint4*>(ktile + kt_swz<HD>(u * 16 + i, 4 * t + q));
+      ka[u][t] = *reinterpret_cast<const uint4*>(ktile + (u * 16 + i) * RB +
+                                                 (((4 * t + q) ^ fi) << 4));
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[t]), qb[t], acc);
+    for (int t = 0; t < T; ++t) acc = mfma16(as_bf16x8(ka[u][t]), qb[t], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[u * 4 + r] = kvalid[u][r] ? acc[r] : -INFINITY;
+  }
+  // value tile rows: first half keys 4q+k, second half 16+4q+k; this lane
+  // (4k + c within its 16-lane group) reads row 4q + i/4, bytes 8 * (i % 4)
+  // of each 32-byte piece
+  const int row0 = 4 * q + (i >> 2);
+  const int vb = row0 * RB + ((((i & 3) >> 1) ^ sp_f<HD>(row0)) << 4) + (i & 1) * 8;
+  uint4 vv[HD / 16];
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) {
+    const uint2 lo = lds_tr(vtile, vb ^ (dt << 5));
+    const uint2 hi = lds_tr(vtile, (vb ^ (dt << 5)) + 16 * RB);
+    vv[dt].x = lo.x; vv[dt].y = lo.y; vv[dt].z = hi.x; vv[dt].w = hi.y;
   }
   float mt = s[0];
 #pragma unroll
@@ -167,16 +206,8 @@ __device__ __forceinline__ void step32_lds(const char* ktile, const char* vtile,
   for (int x = 0; x < 8; ++x) ps += p[x];
   st.l += ps;
   const bf16x8 pb = pack8(p);
-  const int row0 = 4 * q + (i >> 2);
-  const int colb = (i & 3) * 8;
 #pragma unroll
-  for (int dt = 0; dt < HD / 16; ++dt) {
-    const uint2 lo = lds_tr(vtile, vt_swz<HD>(row0, dt * 32 + colb));
-    const uint2 hi = lds_tr(vtile, vt_swz<HD>(16 + row0, dt * 32 + colb));
-    uint4 u;
-    u.x = lo.x; u.y = lo.y; u.z = hi.x; u.w = hi.y;
-    st.o[dt] = mfma16(as_bf16x8(u), pb, st.o[dt]);
-  }
+  for (int dt = 0; dt < HD / 16; ++dt) st.o[dt] = mfma16(as_bf16x8(vv[dt]), pb, st.o[dt]);
 }
 
 }  // namespace dsa
