@@ -503,7 +503,9 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
       for (int s0 = lo; s0 < hi; s0 += kSeg) {
         const int sn = min(kSeg, hi - s0);
         // stage this part of the segment, each entry checked against the range
-        // and the row (entries past the segment read as -1)
+        // and the row (entries past the segment read as -1): the byte offset
+        // of the entry's row, or INT_MIN for an entry outside this range
+        // (less than 2^31 by the launch's limit on L * Hkv * d * 2)
         int jv[kSeg / 64];
 #pragma unroll
         for (int x = 0; x < kSeg / 64; ++x) {
@@ -512,9 +514,8 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
         }
 #pragma unroll
         for (int x = 0; x < kSeg / 64; ++x) {
-          int j = jv[x];
-          if (j < kb || j >= ke) j = -1;
-          wl[x * 64 + lane] = j;
+          const int j = jv[x];
+          wl[x * 64 + lane] = (j >= kb && j < ke) ? (int)((uint32_t)j * rs_bytes) : INT_MIN;
         }
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
@@ -524,7 +525,10 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
         // offsets) while step e0 - 32 computes, then written to the wave's
         // LDS tiles (chunks permuted by sp_f) and read back as MFMA
         // operands.  Lane group gi = lane / CPR stages rows gi * RPG ..
-        // gi * RPG + RPG - 1.  Entries of -1 read row 0 (masked).
+        // gi * RPG + RPG - 1.  Masked entries (INT_MIN) read row 0.  The
+        // loads' register results order the staging stores after them; the
+        // stores and the step's reads of the tiles are LDS operations of one
+        // wave, which the LDS performs in order.
         u32x4 kr[RPG], vr[RPG];
         {
           int jr[RPG];
@@ -533,13 +537,12 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
             *reinterpret_cast<int4*>(&jr[m]) = *reinterpret_cast<const int4*>(wl + gi * RPG + m);
 #pragma unroll
           for (int m = 0; m < RPG; ++m) {
-            const uint32_t off = ((uint32_t)max(jr[m], 0) * rs_bytes) | (cfix ^ (uint32_t)(sp_f<HD>(m) << 4));
+            const uint32_t off = ((uint32_t)jr[m] & 0x7fffffffu) | (cfix ^ (uint32_t)(sp_f<HD>(m) << 4));
             kr[m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
             vr[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
           }
         }
         for (int e0 = 0; e0 < sn; e0 += 32) {
-          __builtin_amdgcn_s_waitcnt(0);   // this step's rows are in registers
 #pragma unroll
           for (int m = 0; m < RPG; ++m) {
             *reinterpret_cast<u32x4*>(kst + m * (HD * 2)) = kr[m];
@@ -552,7 +555,6 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
             kval[u][0] = e4.x >= 0; kval[u][1] = e4.y >= 0;
             kval[u][2] = e4.z >= 0; kval[u][3] = e4.w >= 0;
           }
-          __builtin_amdgcn_s_waitcnt(0);   // tiles written
           __builtin_amdgcn_wave_barrier();
           if (e0 + 32 < sn) {
             int jr[RPG];
@@ -562,7 +564,7 @@ __device__ void sparse_block(const SliceArgs& a, int b, int g, int c, int r0, ch
                   *reinterpret_cast<const int4*>(wl + e0 + 32 + gi * RPG + m);
 #pragma unroll
             for (int m = 0; m < RPG; ++m) {
-              const uint32_t off = ((uint32_t)max(jr[m], 0) * rs_bytes) | (cfix ^ (uint32_t)(sp_f<HD>(m) << 4));
+              const uint32_t off = ((uint32_t)jr[m] & 0x7fffffffu) | (cfix ^ (uint32_t)(sp_f<HD>(m) << 4));
               kr[m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
               vr[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
             }
