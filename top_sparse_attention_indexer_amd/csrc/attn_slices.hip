@@ -267,10 +267,19 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
     }
   }
   ColState<HD> st[2];
+  // softmax denominators on the matrix cores: an all-ones A operand against
+  // the same P^T operand the output MFMA takes gives every lane its
+  // column's sum of the (bf16) weights, so the VALU does no per-score adds
+  // and numerator and denominator use the same rounded weights
+  f32x4 lacc[2];
+  bf16x8 ones;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) ones[x] = (__bf16)1.0f;
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     st[cc].m = -INFINITY;
     st[cc].l = 0.f;
+    lacc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt) st[cc].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -356,14 +365,14 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sv[u * 4 + rr] = sacc[cc][u][rr];
         } else {
-          const int lim = min(prow[cc] + 1, ke);   // keys below lim are visible
+          // keys below lim are visible; key j0 + 4q + (16u + rr) is this
+          // lane's score [u][rr]
+          const int dl = min(prow[cc] + 1, ke) - j0 - 4 * q;
 #pragma unroll
           for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int j = j0 + u * 16 + 4 * q + rr;
-              sv[u * 4 + rr] = j < lim ? sacc[cc][u][rr] : -INFINITY;
-            }
+            for (int rr = 0; rr < 4; ++rr)
+              sv[u * 4 + rr] = u * 16 + rr < dl ? sacc[cc][u][rr] : -INFINITY;
         }
         float mt = sv[0];
 #pragma unroll
@@ -378,7 +387,8 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
           for (int dt = 0; dt < HD / 16; ++dt)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) st[cc].o[dt][rr] *= alpha;
-          st[cc].l *= alpha;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) lacc[cc][rr] *= alpha;
           st[cc].m = mnew;
         }
         // a column whose maximum is still -inf has only masked scores, which
@@ -387,12 +397,10 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
         float pv[16];
 #pragma unroll
         for (int x = 0; x < 16; ++x) pv[x] = exp2_fast(fmaf(sv[x], a.scale_log2, -msub));
-        float ps = 0.f;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) ps += pv[x];
-        st[cc].l += ps;
         pb[cc][0] = pack8(pv);
         pb[cc][1] = pack8(pv + 8);
+        lacc[cc] = mfma16(ones, pb[cc][0], lacc[cc]);
+        lacc[cc] = mfma16(ones, pb[cc][1], lacc[cc]);
       }
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
@@ -418,7 +426,7 @@ __device__ void dense_tile(const SliceArgs& a, int b, int h, int tile, int c, ch
   }
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
-    float l = sum_xor32(sum_xor16(st[cc].l));
+    const float l = lacc[cc][0];
     if (rvalid[cc]) {
       const int r = rbase + w * 32 + cc * 16 + i;
       emit_col<HD>(a, st[cc], l, b, r, h, c, prow[cc] / a.RC + 1);
