@@ -301,6 +301,12 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* scratch) {
   return total;
 }
 
+// Word of bin b in the selection histogram: one pad word after every 32
+// bins, so that lanes reading 32 consecutive bins each (lane l the chunk of
+// bins 32 c_l .. 32 c_l + 31, word 33 c_l + j) hit different LDS banks.
+constexpr int kHistWords = 2048 + 64;
+__device__ __forceinline__ int hslot(uint32_t b) { return (int)(b + (b >> 5)); }
+
 // The kk-th largest (1 <= kk <= m) of the order values get(0), ..., get(n - 1)
 // (key << 32 | ~position, distinct; 0 marks an empty slot, so a value is
 // present iff its low word is nonzero).  m values are present, their keys
@@ -311,8 +317,9 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* scratch) {
 // ranking them.  Each level costs two barriers: wave 0 alone turns the
 // histogram into the digit (32 bins per lane, one DPP scan) and clears the
 // bins it read.
-// Caller: buf[0 .. DT) and res[2] must be zero and hist[0 .. 2048) either zero
-// or, with hist_ready, the counts of the first digit, all visible to every
+// Caller: buf[0 .. DT) and res[2] must be zero and hist[0 .. kHistWords) either
+// zero or, with hist_ready, the counts of the first digit (bin b at word
+// hslot(b)), all visible to every
 // thread (written before a barrier).  On return hist is zero again; buf and
 // res[2] are not.
 // LDS: hist (2048 words), buf (DT values), red (1 value), res (4 words).
@@ -335,12 +342,12 @@ __device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, uin
   };
   const int lane = threadIdx.x & 63;
   uint64_t prefix = 0;   // (value - (hmin << 32)) >> hi of the kk-th
+  const uint64_t hbase = (uint64_t)hmin << 32;
+  // a present value whose digits above bit hi equal the prefix (all present
+  // values while hi = 64; keys are at least hmin, so the difference is the
+  // offset of the value above hbase)
   auto matches = [&](uint64_t v) -> bool {
-    const uint32_t lo = (uint32_t)v, kd = (uint32_t)(v >> 32) - hmin;
-    if (lo == 0) return false;
-    if (hi >= 64) return true;
-    if (hi >= 32) return (kd >> (hi - 32)) == (uint32_t)prefix;
-    return ((((uint64_t)kd << 32) | lo) >> hi) == prefix;
+    return (uint32_t)v != 0u && (hi >= 64 || ((v - hbase) >> hi) == prefix);
   };
   while (m > (uint32_t)DT && hi > 0) {
     const int bits = min(11, hi);
@@ -352,65 +359,54 @@ __device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, uin
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const uint64_t v = vv[x];
-        if (matches(v)) {
-          const uint32_t kd = (uint32_t)(v >> 32) - hmin;
-          const uint32_t dg = sh >= 32 ? (kd >> (sh - 32)) & nbm
-                                       : (uint32_t)(((((uint64_t)kd) << 32) | (uint32_t)v) >> sh) & nbm;
-          atomicAdd(&hist[dg], 1u);
-        }
+        if (matches(v)) atomicAdd(&hist[hslot((uint32_t)((v - hbase) >> sh) & nbm)], 1u);
       }
     }
     __syncthreads();
     if (threadIdx.x < 64) {
-      // lane l holds bins [top_l - per, top_l), lane 0 the highest
+      // lane l holds bins [top_l - per, top_l), lane 0 the highest; an
+      // inclusive scan of the lanes' counts finds the lane whose bins hold
+      // the kk-th value from the top, a second scan over that lane's bins
+      // (one per lane) the bin.  The bins read are cleared.
       const int nb = 1 << bits;
       const int per = max(1, nb >> 6);
       const int top = nb - per * lane;
-      uint32_t hv[32];
+      uint32_t sum = 0;
       if (per == 32) {
-        uint4* hp = reinterpret_cast<uint4*>(hist + top - 32);
-        uint4 u8[8];
+        // an 11-bit digit: bins top - 32 .. top - 1, all reads in flight together
+        uint32_t hv[32];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) u8[q] = hp[q];
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 32; ++j) hv[j] = hist[hslot((uint32_t)(top - 32 + j))];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint4 u4 = u8[q];
-          hv[31 - 4 * q] = u4.x;
-          hv[30 - 4 * q] = u4.y;
-          hv[29 - 4 * q] = u4.z;
-          hv[28 - 4 * q] = u4.w;
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) hp[q] = make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < 32; ++j) sum += hv[j];
       } else {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
+#pragma unroll 1
+        for (int j = 0; j < per; ++j) {
           const int bin = top - 1 - j;
-          hv[j] = (j < per && bin >= 0) ? hist[bin] : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const int bin = top - 1 - j;
-          if (j < per && bin >= 0) hist[bin] = 0;
+          sum += bin >= 0 ? hist[hslot((uint32_t)bin)] : 0u;
         }
       }
-      uint32_t sum = 0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) sum += hv[j];
       const uint32_t incl = wave_incl_scan(sum);          // values in bins >= this lane's lowest
-      const uint64_t hit = __ballot(incl >= kk);
-      const int L = __ffsll((long long)hit) - 1;
-      if (lane == L) {
-        uint32_t above = incl - sum;
+      const int L = __ffsll((long long)__ballot(incl >= kk)) - 1;
+      const int topL = __builtin_amdgcn_readlane(top, L);
+      const uint32_t aboveL = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
+      const int bin = topL - 1 - lane;
+      const uint32_t cnt = (lane < per && bin >= 0) ? hist[hslot((uint32_t)bin)] : 0u;
+      const uint32_t ci = aboveL + wave_incl_scan(cnt);
+      const int J = __ffsll((long long)__ballot(ci >= kk)) - 1;
+      if (lane == J) {
+        res[0] = (uint32_t)bin;
+        res[1] = ci - cnt;
+        res[3] = cnt;
+      }
+      if (per == 32) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          if (j < per && above < kk && above + hv[j] >= kk) {
-            res[0] = (uint32_t)(top - 1 - j);
-            res[1] = above;
-            res[3] = hv[j];
-          }
-          above += hv[j];
+        for (int j = 0; j < 32; ++j) hist[hslot((uint32_t)(top - 32 + j))] = 0u;
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < per; ++j) {
+          const int b2 = top - 1 - j;
+          if (b2 >= 0) hist[hslot((uint32_t)b2)] = 0u;
         }
       }
     }
@@ -424,7 +420,7 @@ __device__ __forceinline__ uint64_t kth_largest(int n, uint32_t kk, Get get, uin
   }
   if (hist_ready) {
     // counts handed in but no level needed: leave the histogram cleared
-    for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+    for (int i = threadIdx.x; i < kHistWords; i += DT) hist[i] = 0;
   }
   // gather: one LDS atomic per wave and group of eight values for the slots
   for (int k = 0; k < iters; ++k) {
@@ -873,7 +869,7 @@ template <typename TI, int DIDX, typename TQ, int HD, int HCT>
 __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
   __shared__ float4 lds4[kLdsFloats / 4];
   float* lds = reinterpret_cast<float*>(lds4);
-  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t hist[kHistWords];
   __shared__ uint32_t scratch[DT / DSA_WAVE + 1];
   __shared__ uint32_t res[4];
   __shared__ int flag;
@@ -944,7 +940,7 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
   if (!has_unit) return;   // a workgroup without a chunk has no further work
   if (a.M) {
     // state the candidate selection expects (published by the barriers below)
-    for (int i = threadIdx.x; i < 2048; i += DT) hist[i] = 0;
+    for (int i = threadIdx.x; i < kHistWords; i += DT) hist[i] = 0;
     reinterpret_cast<uint64_t*>(lds + a.CH)[threadIdx.x] = 0;
     if (threadIdx.x == 0) res[2] = 0;
   }
@@ -1535,12 +1531,8 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
           const int i = i0 + x * DT + (int)threadIdx.x;
           const uint64_t v = v16[x];
           if (i < a.Cpad) cbuf[i] = v;
-          if ((uint32_t)v != 0u) {
-            const uint32_t kd = (uint32_t)(v >> 32) - kmin;
-            const uint32_t dg = sh >= 32 ? (kd >> (sh - 32)) & nbm
-                                         : (uint32_t)(((((uint64_t)kd) << 32) | (uint32_t)v) >> sh) & nbm;
-            atomicAdd(&hist[dg], 1u);
-          }
+          if ((uint32_t)v != 0u)
+            atomicAdd(&hist[hslot((uint32_t)((v - ((uint64_t)kmin << 32)) >> sh) & nbm)], 1u);
         }
       }
       const uint64_t ck =
@@ -1551,28 +1543,36 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
       if (c == 0 && threadIdx.x == 0)
         st_dev64(a.verdict + 8 * b, ((uint64_t)ep << 32) | (valid ? 1u : 2u));
       if (valid) {
-        // thread t takes entries [t * per, (t + 1) * per), per <= 32 and even
-        const int per = a.Cpad / DT;
-        const uint64_t* mine = cbuf + (size_t)threadIdx.x * per;
-        uint32_t sel = 0;
-        typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-        u64x2 v2[16];
+        // the list: the candidates at or above cK in position order.  Wave
+        // w takes entries [w * Cpad / 4, (w + 1) * Cpad / 4) in rounds of 64
+        // consecutive ones (a count pass, a scan of the four waves' counts,
+        // then the write pass with lane offsets from the round's ballot)
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int span = a.Cpad / 4;                   // a multiple of 256
+        const uint64_t* wsrc = cbuf + (size_t)w * span + lane;
+        uint32_t cntw = 0;
+        for (int r0 = 0; r0 < span; r0 += 64 * 4) {
+          uint64_t v4[4];
 #pragma unroll
-        for (int x = 0; x < 32; x += 2)
-          v2[x / 2] = *reinterpret_cast<const u64x2*>(mine + min(x, per - 2));
-        __builtin_amdgcn_sched_barrier(0);
+          for (int x = 0; x < 4; ++x) v4[x] = wsrc[r0 + 64 * x];
 #pragma unroll
-        for (int x = 0; x < 32; x += 2) {
-          const bool in = x < per;
-          sel |= (in && v2[x / 2].x >= ck ? 1u : 0u) << x;
-          sel |= (in && v2[x / 2].y >= ck ? 1u : 0u) << (x + 1);
+          for (int x = 0; x < 4; ++x) cntw += (uint32_t)__popcll(__ballot(v4[x] >= ck));
         }
-        uint32_t tot;
-        uint32_t o = block_excl_scan<DT>((uint32_t)__popc(sel), scratch, tot);
-        while (sel) {
-          const int x = __ffs(sel) - 1;
-          sel &= sel - 1;
-          llw[o++] = ~(uint32_t)mine[x];
+        if (lane == 0) scratch[w] = cntw;
+        __syncthreads();
+        uint32_t o = 0;
+        for (int x = 0; x < w; ++x) o += scratch[x];
+        for (int r0 = 0; r0 < span; r0 += 64 * 4) {
+          uint64_t v4[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v4[x] = wsrc[r0 + 64 * x];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const bool in = v4[x] >= ck;
+            const uint64_t mk = __ballot(in);
+            if (in) llw[o + (uint32_t)__popcll(mk & lanemask_lt())] = ~(uint32_t)v4[x];
+            o += (uint32_t)__popcll(mk);
+          }
         }
         __syncthreads();
         llist = llw;
