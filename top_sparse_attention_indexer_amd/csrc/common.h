@@ -65,6 +65,25 @@ __device__ __forceinline__ uint32_t wave_incl_dpp(uint32_t x, uint32_t ident, Op
   return x;
 }
 
+// Sum over each aligned group of G lanes (G = 2, 4, 8 or 16) on the DPP
+// network, every lane of the group getting the sum: swaps of neighbours and
+// of lane pairs within each quad, then the mirror of each half row (quad 0
+// with quad 1) and of each row (its halves).  The pairs combined at each step
+// hold equal partial sums in both lanes, so every lane of a group ends with
+// the same bits.
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "lane groups of 2 to 16");
+#define DSA_DPP_ADD(v, ctrl) \
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, false))
+  DSA_DPP_ADD(x, 0xb1);                           // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) DSA_DPP_ADD(x, 0x4e);     // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) DSA_DPP_ADD(x, 0x141);    // row_half_mirror
+  if constexpr (G >= 16) DSA_DPP_ADD(x, 0x140);   // row_mirror
+#undef DSA_DPP_ADD
+  return x;
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return wave_incl_dpp(x, 0u, [](uint32_t p, uint32_t q) { return p + q; });

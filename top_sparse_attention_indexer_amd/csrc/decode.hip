@@ -930,8 +930,12 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
           float s = 0.f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) s = fmaf(qv[n][e], kv[e], s);
+          if constexpr (LPK <= 16) {
+            s = group_sum_dpp<LPK>(s);
+          } else {
 #pragma unroll
-          for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+            for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+          }
           if (sub == 0 && jj < clen) lds[n * a.CH + jj] = s;
         }
       }

@@ -297,9 +297,13 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
       for (int x = 0; x < 4; ++x) bits |= (j0 + 4 * q + x < lim && acc[x] >= tau) ? (1u << x) : 0u;
       const uint32_t c = __popc(bits);
       // counts of the column's quads (lane 16 q + i): prefix over q
-      const uint32_t c1 = __shfl_xor(c, 16, 64);            // quad q ^ 1
+      // the partner lanes' counts by the gfx950 lane swaps (VALU, no LDS
+      // round trip): each swap hands both lanes of a pair both values
+      const auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+      const uint32_t c1 = (q & 1) ? s16[0] : s16[1];         // quad q ^ 1
       const uint32_t pair = c + c1;
-      const uint32_t pair2 = __shfl_xor(pair, 32, 64);      // the other pair
+      const auto s32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+      const uint32_t pair2 = (q & 2) ? s32[0] : s32[1];      // the other pair
       if (WRITE) {
         const uint32_t before = ((q & 1) ? c1 : 0u) + ((q & 2) ? pair2 : 0u);
         uint32_t slot = (uint32_t)run + before;
