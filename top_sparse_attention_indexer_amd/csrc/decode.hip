@@ -910,7 +910,7 @@ __global__ __launch_bounds__(DT, 2) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
         qv[n][e] = (n < N) ? ld_f(qi, ((size_t)b * N + n) * DIDX + sub * EPL + e) : 0.f;
-    constexpr int U = 16;
+    constexpr int U = 8;
     for (int base = w * KPW; base < clen; base += 4 * KPW * U) {
       uint4 raw[U];
 #pragma unroll
