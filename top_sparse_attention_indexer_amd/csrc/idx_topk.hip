@@ -447,6 +447,7 @@ __global__ __launch_bounds__(CT) void k_topk_cands(SelectArgs a) {
   __shared__ uint32_t ckey[kCandLds];
   __shared__ float sc[16 * (CT / 64)];
   __shared__ uint32_t scratch[CT / 64 + 1];
+  __shared__ uint32_t wcnt[2 * (CT / 64)];
   __shared__ uint32_t res[2];
   const int r = blockIdx.x, b = blockIdx.y;
   const int n = a.n0 + r;
@@ -502,20 +503,48 @@ __global__ __launch_bounds__(CT) void k_topk_cands(SelectArgs a) {
   pick_bin_ct(hist, 1024, kk, scratch, res);
   const uint32_t Tk = (pfx << 10) | res[0];
   kk -= res[1];   // keys equal to Tk still to take, lowest positions first
-  // ordered compaction: the list is in position order
-  uint32_t base_sel = 0, base_tie = 0;
-  for (int x0 = 0; x0 < cnt; x0 += CT) {
-    const int x = x0 + (int)threadIdx.x;
-    const bool in = x < cnt;
-    const uint32_t u = in ? ckey[x] : 0u;
-    const bool gt = in && u > Tk, eq = in && u == Tk;
-    uint32_t tie_tot, sel_tot;
-    const uint32_t tie_rank = block_rank<CT>(eq, scratch, tie_tot);
-    const bool sel = gt || (eq && base_tie + tie_rank < kk);
-    const uint32_t pos = block_rank<CT>(sel, scratch, sel_tot);
-    if (sel && base_sel + pos < (uint32_t)a.K) o[base_sel + pos] = __float_as_int(cl[x].y);
-    base_tie += tie_tot;
-    base_sel += sel_tot;
+  // ordered compaction (the list is in position order).  Wave w takes the
+  // entries [w * span, (w + 1) * span) in rounds of 64: a count pass of its
+  // keys above Tk and equal to Tk, one exchange of the waves' counts, then
+  // the write pass.  An entry's output slot is the number of selected
+  // entries before it: every key above Tk, and the first kk keys equal to Tk.
+  {
+    constexpr int NW = CT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int span = (cnt + NW * 64 - 1) / (NW * 64) * 64;
+    const int xb = w * span, xe = min(cnt, xb + span);
+    uint32_t ngt = 0, neq = 0;
+    for (int x0 = xb; x0 < xe; x0 += 64) {
+      const int x = x0 + lane;
+      const uint32_t u = x < xe ? ckey[x] : 0u;
+      ngt += (uint32_t)__popcll(__ballot(x < xe && u > Tk));
+      neq += (uint32_t)__popcll(__ballot(x < xe && u == Tk));
+    }
+    if (lane == 0) {
+      wcnt[w] = ngt;
+      wcnt[NW + w] = neq;
+    }
+    __syncthreads();
+    uint32_t gtb = 0, tb = 0;   // keys above / equal to Tk before this wave's span
+    for (int v = 0; v < w; ++v) {
+      gtb += wcnt[v];
+      tb += wcnt[NW + v];
+    }
+    const uint64_t below = lanemask_lt();
+    for (int x0 = xb; x0 < xe; x0 += 64) {
+      const int x = x0 + lane;
+      const bool in = x < xe;
+      const uint32_t u = in ? ckey[x] : 0u;
+      const bool gt = in && u > Tk, eq = in && u == Tk;
+      const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
+      const uint32_t g0 = gtb + (uint32_t)__popcll(mgt & below);
+      const uint32_t t0l = tb + (uint32_t)__popcll(meq & below);
+      const bool sel = gt || (eq && t0l < kk);
+      const uint32_t pos = g0 + min(t0l, kk);
+      if (sel && pos < (uint32_t)a.K) o[pos] = __float_as_int(cl[x].y);
+      gtb += (uint32_t)__popcll(mgt);
+      tb += (uint32_t)__popcll(meq);
+    }
   }
 }
 
