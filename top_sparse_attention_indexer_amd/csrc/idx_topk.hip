@@ -13,7 +13,8 @@
 //     score range and a 256-bin histogram; the threshold tau is the lower
 //     edge of the bin that brings the count from the top to about
 //     1.5 K * samples / visible (no threshold when that covers every key).
-//   k_idx_scan<false>: workgroups of 64 rows x 256 keys count, per (row, key
+//   k_idx_scan<false>: workgroups of 128 rows x 256 keys (each wave two
+//     16-row MFMA column blocks on one key operand) count, per (row, key
 //     chunk), the scores >= tau; k_idx_offsets turns the counts into each
 //     chunk's offset in the row's candidate list;
 //   k_idx_scan<true>: the same tiles again, appending (score, position) of
@@ -34,6 +35,7 @@ namespace {
 
 constexpr int FT = 256;           // threads of the filter (4 waves)
 constexpr int kRowsPerWg = 64;
+constexpr int kScanRows = 128;     // rows per scan workgroup (two 16-row blocks per wave)
 constexpr int kSamples = 2048;    // sampled keys per row (at most)
 constexpr int kBins = 256;
 constexpr int CT = 512;           // threads of the selection
@@ -209,13 +211,14 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
   constexpr int T = DIDX / 32;
   constexpr int CPR = DIDX / 8;                  // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;                  // key rows per direct load
+  constexpr int RB = kScanRows / 64;             // 16-row blocks per wave
   __shared__ __attribute__((aligned(16))) char ktile[KC * DIDX * 2];
   const int b = blockIdx.z, kc = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 4, i = lane & 15;
-  const int rb0 = blockIdx.x * kRowsPerWg;
+  const int rb0 = blockIdx.x * kScanRows;
   // block-uniform exits: the block's last row bounds the keys it scans
-  const int p_blk = a.L - a.N + (a.n0 + min(a.R - 1, rb0 + kRowsPerWg - 1)) / a.rpt;
+  const int p_blk = a.L - a.N + (a.n0 + min(a.R - 1, rb0 + kScanRows - 1)) / a.rpt;
   const int j_lo = kc * KC;
   if (j_lo > p_blk || p_blk + 1 <= a.K || !any_sparse(a.route, b, a.Hq)) return;
   const int j_hi = min(j_lo + KC, p_blk + 1);   // keys [j_lo, j_hi) of this tile
@@ -230,92 +233,117 @@ __global__ __launch_bounds__(FT) void k_idx_scan(FilterArgs a) {
                                      (__attribute__((address_space(3))) void*)(ktile + m * 1024),
                                      16, 0, 0);
   }
-  const int r0 = rb0 + w * 16;
-  const int r = r0 + i;
-  const bool rv = r < a.R;
-  const size_t row = (size_t)b * a.R + (rv ? r : 0);
-  const int p = a.L - a.N + (a.n0 + (rv ? r : 0)) / a.rpt;
-  const bool need = rv && p + 1 > a.K && j_lo <= p;
-  const float tau = need ? a.tau[row] : INFINITY;
-  bf16x8 qb[T];
-  {
+  // this wave's rows: block u holds rows r0 + 16 u + i (one MFMA column each)
+  const int r0 = rb0 + w * 16 * RB;
+  bool need[RB];
+  float tau[RB];
+  int lim[RB];                                    // keys below lim are visible
+  size_t row[RB];
+  bf16x8 qb[RB][T];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    const int r = r0 + 16 * u + i;
+    const bool rv = r < a.R;
+    row[u] = (size_t)b * a.R + (rv ? r : 0);
+    const int p = a.L - a.N + (a.n0 + (rv ? r : 0)) / a.rpt;
+    need[u] = rv && p + 1 > a.K && j_lo <= p;
+    // a row without a list has tau = +inf, so no score passes it
+    tau[u] = need[u] ? a.tau[row[u]] : INFINITY;
+    lim[u] = need[u] ? p + 1 : 0;
     const bf16_bits* qr = a.q_idx + ((size_t)b * a.N * a.rpt + a.n0 + (rv ? r : 0)) * DIDX;
 #pragma unroll
     for (int t = 0; t < T; ++t)
-      qb[t] = as_bf16x8(rv ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
-                           : make_uint4(0, 0, 0, 0));
+      qb[u][t] = as_bf16x8(rv ? *reinterpret_cast<const uint4*>(qr + t * 32 + q * 8)
+                              : make_uint4(0, 0, 0, 0));
   }
-  int32_t* cc = a.ccnt + row * a.nkc + kc;
-  int run = 0;
-  if (WRITE) run = need ? *cc : 0;
-  float2* clist = a.cand + row * a.cap;
+  int run[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) run[u] = (WRITE && need[u]) ? a.ccnt[row[u] * a.nkc + kc] : 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();                               // the whole tile has landed
   // this wave's rows see keys up to p_w; keys up to p_w0 (its first row's
   // position) are visible to every row of the wave (wave-uniform values)
-  const int p_w = __builtin_amdgcn_readfirstlane(a.L - a.N + (a.n0 + min(a.R - 1, r0 + 15)) / a.rpt);
+  const int p_w = __builtin_amdgcn_readfirstlane(
+      a.L - a.N + (a.n0 + min(a.R - 1, r0 + 16 * RB - 1)) / a.rpt);
   const int p_w0 = __builtin_amdgcn_readfirstlane(a.L - a.N + (a.n0 + r0) / a.rpt);
-  // a row without a list has tau = +inf, so no score passes it
-  const int lim = need ? p + 1 : 0;                // keys below lim are visible
+  // the scores of a 16-key block for both row blocks, the key operand read
+  // from LDS once
+  auto scores = [&](int j0, f32x4 (&acc)[RB]) __attribute__((always_inline)) {
+    const int u16 = (j0 - j_lo) >> 4;
+    uint4 kv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      kv[t] = *reinterpret_cast<const uint4*>(ktile + kt_swz<DIDX>(u16 * 16 + i, 4 * t + q));
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[u] = mfma16(as_bf16x8(kv[t]), qb[u][t], acc[u]);
+    }
+  };
   if (!WRITE) {
     // counts only: per lane over the tiles, across the quads once at the end
-    uint32_t cnt = 0;
+    uint32_t cnt[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) cnt[u] = 0;
     if (r0 < a.R && j_lo <= p_w) {
       for (int j0 = j_lo; j0 < j_hi && j0 <= p_w; j0 += 16) {
-        const int u = (j0 - j_lo) >> 4;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(ktile + kt_swz<DIDX>(u * 16 + i, 4 * t + q));
-          acc = mfma16(as_bf16x8(kv), qb[t], acc);
-        }
+        f32x4 acc[RB];
+        scores(j0, acc);
         if (j0 + 15 <= p_w0) {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) cnt += acc[x] >= tau ? 1u : 0u;
+          for (int u = 0; u < RB; ++u)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) cnt[u] += acc[u][x] >= tau[u] ? 1u : 0u;
         } else {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) cnt += (j0 + 4 * q + x < lim && acc[x] >= tau) ? 1u : 0u;
+          for (int u = 0; u < RB; ++u)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              cnt[u] += (j0 + 4 * q + x < lim[u] && acc[u][x] >= tau[u]) ? 1u : 0u;
         }
       }
     }
-    cnt += __shfl_xor(cnt, 16, 64);
-    cnt += __shfl_xor(cnt, 32, 64);
-    if (need && q == 0) *cc = (int)cnt;
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      uint32_t c = cnt[u];
+      c += __shfl_xor(c, 16, 64);
+      c += __shfl_xor(c, 32, 64);
+      if (need[u] && q == 0) a.ccnt[row[u] * a.nkc + kc] = (int)c;
+    }
     return;
   }
   if (r0 < a.R && j_lo <= p_w) {
     for (int j0 = j_lo; j0 < j_hi && j0 <= p_w; j0 += 16) {
-      const int u = (j0 - j_lo) >> 4;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[RB];
+      scores(j0, acc);
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(ktile + kt_swz<DIDX>(u * 16 + i, 4 * t + q));
-        acc = mfma16(as_bf16x8(kv), qb[t], acc);
-      }
-      uint32_t bits = 0;
+      for (int u = 0; u < RB; ++u) {
+        uint32_t bits = 0;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) bits |= (j0 + 4 * q + x < lim && acc[x] >= tau) ? (1u << x) : 0u;
-      const uint32_t c = __popc(bits);
-      // counts of the column's quads (lane 16 q + i): prefix over q
-      // the partner lanes' counts by the gfx950 lane swaps (VALU, no LDS
-      // round trip): each swap hands both lanes of a pair both values
-      const auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
-      const uint32_t c1 = (q & 1) ? s16[0] : s16[1];         // quad q ^ 1
-      const uint32_t pair = c + c1;
-      const auto s32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
-      const uint32_t pair2 = (q & 2) ? s32[0] : s32[1];      // the other pair
-      if (WRITE) {
+        for (int x = 0; x < 4; ++x)
+          bits |= (j0 + 4 * q + x < lim[u] && acc[u][x] >= tau[u]) ? (1u << x) : 0u;
+        const uint32_t c = __popc(bits);
+        // the partner lanes' counts by the gfx950 lane swaps (VALU, no LDS
+        // round trip): each swap hands both lanes of a pair both values
+        const auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+        const uint32_t c1 = (q & 1) ? s16[0] : s16[1];         // quad q ^ 1
+        const uint32_t pair = c + c1;
+        const auto s32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+        const uint32_t pair2 = (q & 2) ? s32[0] : s32[1];      // the other pair
+        // counts of the column's quads (lane 16 q + i): prefix over q
         const uint32_t before = ((q & 1) ? c1 : 0u) + ((q & 2) ? pair2 : 0u);
-        uint32_t slot = (uint32_t)run + before;
+        uint32_t slot = (uint32_t)run[u] + before;
+        float2* clist = a.cand + row[u] * a.cap;
         while (bits) {
           const int x = __ffs(bits) - 1;
           bits &= bits - 1;
           if (slot < (uint32_t)a.cap)
-            clist[slot] = make_float2(acc[x], __int_as_float(j0 + 4 * q + x));
+            clist[slot] = make_float2(acc[u][x], __int_as_float(j0 + 4 * q + x));
           ++slot;
         }
+        run[u] += (int)(pair + pair2);
       }
-      run += (int)(pair + pair2);
     }
   }
 }
@@ -592,7 +620,8 @@ hipError_t launch_idx_topk(const Dims& D, const void* q_idx, const void* k_idx, 
   sa.rpt = D.IH;
   const int rb = (R + kRowsPerWg - 1) / kRowsPerWg;
   const int nk_used = (D.L - D.N + (n0 + R - 1) / D.IH) / KC + 1;   // chunks the last row sees
-  const dim3 gt(rb, D.B), gscan(rb, nk_used, D.B), gs(R, D.B);
+  const int rbs = (R + kScanRows - 1) / kScanRows;
+  const dim3 gt(rb, D.B), gscan(rbs, nk_used, D.B), gs(R, D.B);
   const dim3 goff((unsigned)((rows + 3) / 4));
   {
     ProfScope ps(s, kStageIndexer);
